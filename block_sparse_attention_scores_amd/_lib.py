@@ -1,0 +1,255 @@
+"""ctypes binding of libsolattn (include/solattn.h): argument marshalling only.
+
+Every step of the pass runs in the library's HIP kernels.  PyTorch supplies device
+memory (inputs, outputs, the workspace) and the current HIP stream.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsolattn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "solattn.h")
+
+OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+BF16, FP32 = 0, 1
+MODE_SOL, MODE_SLA = 0, 1
+MAX_EXTRA = 256
+NKERNELS = 5
+
+
+class SolattnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"libsolattn status {status} ({status_string(status)}): {detail}")
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+        ("q_stride", ctypes.c_int64 * 3),
+        ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3),
+        ("o_stride", ctypes.c_int64 * 3),
+        ("dense_row_begin", ctypes.c_int),
+        ("dense_row_end", ctypes.c_int),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "total", "qbar", "kbar", "vbar", "scores", "kept_cnt", "kept_idx", "mult", "extra_cnt",
+        "extra_idx", "extra_buf", "kbar_bf", "vbar_t", "v_t")] + [
+        ("Mq", ctypes.c_int), ("M", ctypes.c_int), ("Mpad", ctypes.c_int)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m block_sparse_attention_scores_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.sol_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, ctypes.POINTER(Opts)]
+    L.sol_attn_fwd.restype = i
+    L.sla_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, ctypes.POINTER(Opts)]
+    L.sla_attn_fwd.restype = i
+    L.solattn_check_args.argtypes = [i, vp, vp, vp, vp, i, i, i, i, f, f, i, i, i, i, ctypes.POINTER(Opts)]
+    L.solattn_check_args.restype = i
+    L.solattn_workspace_layout.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(WsLayout)]
+    L.solattn_workspace_layout.restype = i
+    L.solattn_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    L.solattn_workspace_bytes.restype = ctypes.c_size_t
+    L.solattn_status_string.argtypes = [i]
+    L.solattn_status_string.restype = ctypes.c_char_p
+    L.solattn_last_error.argtypes = []
+    L.solattn_last_error.restype = ctypes.c_char_p
+    L.solattn_timing_enable.argtypes = [i]
+    L.solattn_timing_enable.restype = i
+    L.solattn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong), i]
+    L.solattn_timing_read.restype = i
+    L.solattn_kernel_name.argtypes = [i]
+    L.solattn_kernel_name.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().solattn_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().solattn_last_error().decode()
+
+
+def kernel_names():
+    return [lib().solattn_kernel_name(k).decode() for k in range(NKERNELS)]
+
+
+def workspace_layout(mode: int, dtype: int, B: int, H: int, N: int, d: int, block_q: int,
+                     block_k: int) -> WsLayout:
+    L = WsLayout()
+    rc = lib().solattn_workspace_layout(mode, dtype, B, H, N, d, block_q, block_k, ctypes.byref(L))
+    if rc != OK:
+        raise SolattnError(rc, "invalid workspace shape")
+    return L
+
+
+def workspace_bytes(mode, dtype, B, H, N, d, block_q, block_k) -> int:
+    return int(lib().solattn_workspace_bytes(mode, dtype, B, H, N, d, block_q, block_k))
+
+
+def make_opts(dtype=BF16, strides=None, dense_rows=(0, 0), workspace=0, workspace_bytes=0,
+              stream=0) -> Opts:
+    o = Opts()
+    o.struct_size = ctypes.sizeof(Opts)
+    o.dtype = dtype
+    if strides is not None:
+        for name, st in zip(("q_stride", "k_stride", "v_stride", "o_stride"), strides):
+            arr = getattr(o, name)
+            for j in range(3):
+                arr[j] = int(st[j])
+    o.dense_row_begin, o.dense_row_end = int(dense_rows[0]), int(dense_rows[1])
+    o.workspace = workspace or None
+    o.workspace_bytes = int(workspace_bytes)
+    o.stream = stream or None
+    return o
+
+
+def timing_enable(on: bool = True) -> None:
+    lib().solattn_timing_enable(1 if on else 0)
+
+
+def timing_read():
+    """{kernel name: (total ms, launches)} since the last read; waits for the recorded events."""
+    ms = (ctypes.c_double * NKERNELS)()
+    n = (ctypes.c_longlong * NKERNELS)()
+    rc = lib().solattn_timing_read(ms, n, NKERNELS)
+    if rc != OK:
+        raise SolattnError(rc, "timing read")
+    return {name: (ms[k], n[k]) for k, name in enumerate(kernel_names())}
+
+
+# ----------------------------------------------------------------------------- torch front end
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check_tensor(name, t, shape, dtype):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != 4 or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} dtype {t.dtype} != {dtype}")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name}: the d axis must be contiguous")
+
+
+def alloc_workspace(mode, q, block_q, block_k):
+    torch = _torch()
+    B, H, N, d = q.shape
+    nbytes = workspace_bytes(mode, _dtype_code(q), B, H, N, d, block_q, block_k)
+    return torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+
+
+def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, extra_tokens,
+          dense_rows, out, workspace, stream):
+    torch = _torch()
+    B, H, N, d = q.shape
+    for n, t in (("k", k), ("v", v)):
+        _check_tensor(n, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape, q.dtype)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _check_tensor("out", out, q.shape, q.dtype)
+    if workspace is None:
+        workspace = alloc_workspace(mode, q, block_q, block_k)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    strides = [tuple(t.stride()[:3]) for t in (q, k, v, out)]
+    opts = make_opts(_dtype_code(q), strides, dense_rows, workspace.data_ptr(),
+                     workspace.numel() * workspace.element_size(), stream)
+    L = lib()
+    if mode == MODE_SOL:
+        rc = L.sol_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
+                            float(tau), block_q, block_k, sink_range, extra_tokens, ctypes.byref(opts))
+    else:
+        rc = L.sla_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
+                            block_q, block_k, sink_range, extra_tokens, float(keep_percent),
+                            ctypes.byref(opts))
+    if rc != OK:
+        raise SolattnError(rc, last_error())
+    return out, workspace
+
+
+def sol_attn(q, k, v, *, tau=1.3, block_q=64, block_k=64, sink_range=0, extra_tokens=0,
+             dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False):
+    """sol-attn forward on [B, H, N, d] GPU tensors (bfloat16 or float32); see include/solattn.h."""
+    o, ws = _call(MODE_SOL, q, k, v, tau=tau, keep_percent=0.0, block_q=block_q, block_k=block_k,
+                  sink_range=sink_range, extra_tokens=extra_tokens, dense_rows=dense_rows, out=out,
+                  workspace=workspace, stream=stream)
+    return (o, ws) if return_workspace else o
+
+
+def sla_attn(q, k, v, *, keep_percent=10.0, block_q=128, block_k=64, sink_range=0, extra_tokens=0,
+             dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False):
+    """sla forward on [B, H, N, d] GPU tensors (bfloat16 or float32); see include/solattn.h."""
+    o, ws = _call(MODE_SLA, q, k, v, tau=0.0, keep_percent=keep_percent, block_q=block_q,
+                  block_k=block_k, sink_range=sink_range, extra_tokens=extra_tokens,
+                  dense_rows=dense_rows, out=out, workspace=workspace, stream=stream)
+    return (o, ws) if return_workspace else o
+
+
+def selection_views(workspace, mode, dtype, B, H, N, d, block_q, block_k):
+    """Views of a call's intermediate results inside its workspace tensor (torch, on device)."""
+    torch = _torch()
+    L = workspace_layout(mode, dtype, B, H, N, d, block_q, block_k)
+    BH, Mq, M, Mpad = B * H, L.Mq, L.M, L.Mpad
+
+    def view(off, count, dt, shape):
+        nbytes = count * torch.tensor([], dtype=dt).element_size()
+        return workspace[off:off + nbytes].view(dt).reshape(shape)
+
+    return dict(
+        qbar=view(L.qbar, BH * Mq * d, torch.float32, (BH, Mq, d)),
+        kbar=view(L.kbar, BH * M * d, torch.float32, (BH, M, d)),
+        vbar=view(L.vbar, BH * M * d, torch.float32, (BH, M, d)),
+        scores=view(L.scores, BH * Mq * M, torch.float32, (BH, Mq, M)),
+        kept_cnt=view(L.kept_cnt, BH * Mq, torch.int32, (BH, Mq)),
+        kept_idx=view(L.kept_idx, BH * Mq * M, torch.int32, (BH, Mq, M)),
+        mult=view(L.mult, BH * Mq * Mpad, torch.uint8, (BH, Mq, Mpad)),
+        extra_cnt=view(L.extra_cnt, BH * Mq, torch.int32, (BH, Mq)),
+        extra_idx=view(L.extra_idx, BH * Mq * MAX_EXTRA, torch.int32, (BH, Mq, MAX_EXTRA)),
+    )
+
+
+def header_functions():
+    """Names of the functions include/solattn.h declares."""
+    import re
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)) - {"if"})

@@ -1,0 +1,78 @@
+"""Build libsolattn.so in-tree with hipcc for gfx950 (no GPU needed to compile).
+
+Usage: python -m block_sparse_attention_scores_amd.build [--jobs N]
+"""
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libsolattn.so")
+SOURCES = ["api.cpp", "pool.hip", "score.hip", "select.hip", "extra.hip", "flash.hip"]
+ARCH = os.environ.get("SOLATTN_ARCH", "gfx950")
+
+COMMON = [
+    "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    # packed fp32 arithmetic stays off: ordinary float code only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-result",
+]
+
+
+def hipcc():
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def build(jobs: int = 8, verbose: bool = False) -> str:
+    cc = hipcc()
+    tmp = tempfile.mkdtemp(prefix="solattn_build_")
+    objs, procs = [], []
+    try:
+        for src in SOURCES:
+            obj = os.path.join(tmp, src.rsplit(".", 1)[0] + ".o")
+            lang = ["-x", "hip"] if src.endswith(".hip") else []
+            cmd = [cc, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+            objs.append(obj)
+            while sum(p.poll() is None for _, p in procs) >= jobs:
+                procs[[p.poll() is None for _, p in procs].index(True)][1].wait()
+        failed = []
+        for src, p in procs:
+            out, _ = p.communicate()
+            text = "\n".join(ln for ln in (out or "").splitlines() if "not a recognized feature" not in ln)
+            if p.returncode != 0:
+                failed.append((src, text))
+            elif verbose and text.strip():
+                print(text)
+        if failed:
+            msg = "\n".join(f"--- {s}\n{t}" for s, t in failed)
+            raise RuntimeError(f"hipcc failed:\n{msg}")
+        tmp_lib = LIB + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}")
+        os.replace(tmp_lib, LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=8)
+    ap.add_argument("-v", "--verbose", action="store_true")
+    a = ap.parse_args()
+    print(build(a.jobs, a.verbose))
+    sys.exit(0)

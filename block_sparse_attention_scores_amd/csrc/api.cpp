@@ -1,0 +1,383 @@
+// libsolattn C ABI: argument validation, workspace planning and the launch sequence
+//   block_pool -> block_score -> block_select -> extra_select -> sparse_flash_fwd
+// on the caller's stream (see include/solattn.h for the contract).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/solattn.h"
+#include "common.h"
+#include "launch.h"
+
+using solattn::Problem;
+using solattn::Tensor;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Strides {
+  int64_t sb, sh, sn;
+};
+
+Strides resolve(const int64_t* s, int H, int N, int d) {
+  if (s[0] == 0 && s[1] == 0 && s[2] == 0) return {(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
+  return {s[0], s[1], s[2]};
+}
+
+// Byte range [lo, hi) touched by a strided tensor.
+void extent(const void* p, Strides s, int B, int H, int N, int d, size_t es, uintptr_t* lo, uintptr_t* hi) {
+  const uintptr_t base = reinterpret_cast<uintptr_t>(p);
+  const int64_t last = (int64_t)(B - 1) * s.sb + (int64_t)(H - 1) * s.sh + (int64_t)(N - 1) * s.sn + (d - 1);
+  *lo = base;
+  *hi = base + static_cast<uintptr_t>(last + 1) * es;
+}
+
+int check(int mode, const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+          float tau, float keep_percent, int block_q, int block_k, int sink_range, int extra_tokens,
+          const solattn_opts* opts, Strides st[4]) {
+  if (mode != SOLATTN_MODE_SOL && mode != SOLATTN_MODE_SLA) return fail(SOLATTN_EINVAL, "mode %d", mode);
+  if (opts && opts->struct_size != (int)sizeof(solattn_opts))
+    return fail(SOLATTN_EINVAL, "opts->struct_size %d != %d", opts->struct_size, (int)sizeof(solattn_opts));
+  const int dtype = opts ? opts->dtype : SOLATTN_BF16;
+  if (dtype != SOLATTN_BF16 && dtype != SOLATTN_FP32) return fail(SOLATTN_EINVAL, "dtype %d", dtype);
+  if (!q || !k || !v || !out) return fail(SOLATTN_EINVAL, "null tensor pointer");
+  if (B < 1 || H < 1 || N < 1 || d < 1) return fail(SOLATTN_EINVAL, "sizes B=%d H=%d N=%d d=%d", B, H, N, d);
+  if (block_q < 1 || block_k < 1) return fail(SOLATTN_EINVAL, "block sizes %d %d", block_q, block_k);
+  if (mode == SOLATTN_MODE_SOL && std::isnan(tau)) return fail(SOLATTN_EINVAL, "tau is NaN");
+  if (mode == SOLATTN_MODE_SLA && !(keep_percent > 0.f && keep_percent <= 100.f))
+    return fail(SOLATTN_EINVAL, "keep_percent %g outside (0, 100]", (double)keep_percent);
+  if (extra_tokens < 0 || extra_tokens > SOLATTN_MAX_EXTRA)
+    return fail(SOLATTN_EINVAL, "extra_tokens %d outside [0, %d]", extra_tokens, SOLATTN_MAX_EXTRA);
+  if (sink_range < 0 || sink_range > N) return fail(SOLATTN_EINVAL, "sink_range %d outside [0, N]", sink_range);
+  const int d0 = opts ? opts->dense_row_begin : 0, d1 = opts ? opts->dense_row_end : 0;
+  if (d0 < 0 || d1 < d0 || d1 > N) return fail(SOLATTN_EINVAL, "dense rows [%d, %d) outside [0, N]", d0, d1);
+
+  const int64_t zero[3] = {0, 0, 0};
+  st[0] = resolve(opts ? opts->q_stride : zero, H, N, d);
+  st[1] = resolve(opts ? opts->k_stride : zero, H, N, d);
+  st[2] = resolve(opts ? opts->v_stride : zero, H, N, d);
+  st[3] = resolve(opts ? opts->o_stride : zero, H, N, d);
+  for (int t = 0; t < 4; ++t)
+    if (st[t].sb < 0 || st[t].sh < 0 || st[t].sn < 0) return fail(SOLATTN_EINVAL, "negative stride");
+  const Strides& so = st[3];
+  if (so.sn < d || (H > 1 && so.sh < (int64_t)N * so.sn) || (B > 1 && so.sb < (int64_t)H * so.sh))
+    return fail(SOLATTN_EINVAL, "out strides make rows overlap");
+  const size_t es = dtype == SOLATTN_BF16 ? 2 : 4;
+  uintptr_t olo, ohi;
+  extent(out, so, B, H, N, d, es, &olo, &ohi);
+  const void* ins[3] = {q, k, v};
+  for (int t = 0; t < 3; ++t) {
+    uintptr_t lo, hi;
+    extent(ins[t], st[t], B, H, N, d, es, &lo, &hi);
+    if (lo < ohi && olo < hi) return fail(SOLATTN_EINVAL, "out overlaps %c", "qkv"[t]);
+  }
+
+  if (d != 64 && d != 128) return fail(SOLATTN_ENOTSUP, "d=%d (this build: 64 or 128)", d);
+  if (block_k != 64) return fail(SOLATTN_ENOTSUP, "block_k=%d (this build: 64)", block_k);
+  if (block_q != 64 && block_q != 128) return fail(SOLATTN_ENOTSUP, "block_q=%d (this build: 64, 128)", block_q);
+  if (N % block_q || N % block_k) return fail(SOLATTN_ENOTSUP, "N=%d not a multiple of the block sizes", N);
+  if (d0 % block_q || d1 % block_q) return fail(SOLATTN_ENOTSUP, "dense rows not block_q aligned");
+  if ((int64_t)B * H > 65535) return fail(SOLATTN_ENOTSUP, "B*H=%lld too large", (long long)B * H);
+  for (int t = 0; t < 4; ++t) {
+    const void* p = t < 3 ? ins[t] : out;
+    if ((reinterpret_cast<uintptr_t>(p) % 16) || ((st[t].sb * es) % 16) || ((st[t].sh * es) % 16) ||
+        ((st[t].sn * es) % 16))
+      return fail(SOLATTN_ENOTSUP, "tensor %c: rows not 16-byte aligned", "qkvo"[t]);
+  }
+  return SOLATTN_OK;
+}
+
+int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k, solattn_ws_layout* L) {
+  (void)mode;
+  if (B < 1 || H < 1 || N < 1 || d < 1 || block_q < 1 || block_k < 1 ||
+      (dtype != SOLATTN_BF16 && dtype != SOLATTN_FP32))
+    return SOLATTN_EINVAL;
+  std::memset(L, 0, sizeof *L);
+  const size_t BH = (size_t)B * H;
+  const int Mq = (N + block_q - 1) / block_q, M = (N + block_k - 1) / block_k;
+  const int Mpad = (M + 63) / 64 * 64;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L->qbar = take(BH * Mq * d * 4);
+  L->kbar = take(BH * M * d * 4);
+  L->vbar = take(BH * M * d * 4);
+  L->scores = take(BH * Mq * M * 4);
+  L->kept_cnt = take(BH * Mq * 4);
+  L->kept_idx = take(BH * Mq * M * 4);
+  L->mult = take(BH * Mq * Mpad);
+  L->extra_cnt = take(BH * Mq * 4);
+  L->extra_idx = take(BH * Mq * SOLATTN_MAX_EXTRA * 4);
+  L->extra_buf = take(BH * Mq * solattn::EXTRA_CAP * 8);
+  if (dtype == SOLATTN_BF16) {
+    L->kbar_bf = take(BH * Mpad * d * 2);
+    L->vbar_t = take(BH * Mpad * d * 2);
+    L->v_t = take(BH * (size_t)M * d * 64 * 2);
+  }
+  L->total = off;
+  L->Mq = Mq;
+  L->M = M;
+  L->Mpad = Mpad;
+  return SOLATTN_OK;
+}
+
+// Library-owned workspace per device (grow-only), used when the caller passes none.
+std::mutex g_ws_mu;
+void* g_ws[64] = {};
+size_t g_ws_size[64] = {};
+
+// Per-kernel timing.
+constexpr int NK = SOLATTN_NKERNELS;
+const char* kKernelNames[NK] = {"block_pool", "block_score", "block_select", "extra_select",
+                                "sparse_flash_fwd"};
+struct TimedCall {
+  hipEvent_t ev[NK + 1];
+  bool ran[NK];
+};
+std::mutex g_t_mu;
+bool g_timing = false;
+std::vector<TimedCall> g_calls;
+std::vector<hipEvent_t> g_free_events;
+
+hipEvent_t take_event() {
+  if (!g_free_events.empty()) {
+    hipEvent_t e = g_free_events.back();
+    g_free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+int run(int mode, const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+        float tau, float keep_percent, int block_q, int block_k, int sink_range, int extra_tokens,
+        const solattn_opts* opts) {
+  g_err.clear();
+  Strides st[4];
+  int rc = check(mode, q, k, v, out, B, H, N, d, tau, keep_percent, block_q, block_k, sink_range,
+                 extra_tokens, opts, st);
+  if (rc != SOLATTN_OK) return rc;
+  const int dtype = opts ? opts->dtype : SOLATTN_BF16;
+  solattn_ws_layout L;
+  layout(mode, dtype, B, H, N, d, block_q, block_k, &L);
+  hipStream_t stream = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
+
+  char* ws = nullptr;
+  if (opts && opts->workspace) {
+    if (opts->workspace_bytes < L.total)
+      return fail(SOLATTN_EWORKSPACE, "workspace %zu bytes < %zu required", opts->workspace_bytes, L.total);
+    if (reinterpret_cast<uintptr_t>(opts->workspace) % 256)
+      return fail(SOLATTN_EINVAL, "workspace not 256-byte aligned");
+    ws = static_cast<char*>(opts->workspace);
+  } else {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(SOLATTN_EHIP, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    if (g_ws_size[dev] < L.total) {
+      if (g_ws[dev]) {
+        hipDeviceSynchronize();
+        hipFree(g_ws[dev]);
+        g_ws[dev] = nullptr;
+        g_ws_size[dev] = 0;
+      }
+      void* p = nullptr;
+      if (hipMalloc(&p, L.total) != hipSuccess) return fail(SOLATTN_EHIP, "hipMalloc(%zu) failed", L.total);
+      g_ws[dev] = p;
+      g_ws_size[dev] = L.total;
+    }
+    ws = static_cast<char*>(g_ws[dev]);
+  }
+
+  Problem P;
+  std::memset(&P, 0, sizeof P);
+  P.B = B; P.H = H; P.N = N; P.d = d;
+  P.bq = block_q; P.bk = block_k;
+  P.Mq = L.Mq; P.M = L.M; P.Mpad = L.Mpad;
+  P.mode = mode; P.dtype = dtype;
+  P.tau = tau;
+  P.keep_all = (mode == SOLATTN_MODE_SOL && std::isinf(tau) && tau < 0) ? 1 : 0;
+  if (mode == SOLATTN_MODE_SLA) {
+    const double kk = std::ceil((double)keep_percent * (double)L.M / 100.0);
+    P.k_sla = kk > L.M ? L.M : (int)kk;
+  }
+  P.sink_blocks = (sink_range + block_k - 1) / block_k;
+  P.extra = extra_tokens;
+  const int d0 = opts ? opts->dense_row_begin : 0, d1 = opts ? opts->dense_row_end : 0;
+  P.dense_q0 = d0 / block_q;
+  P.dense_q1 = d1 / block_q;
+  if (P.dense_q1 <= P.dense_q0) P.dense_q0 = P.dense_q1 = 0;
+  P.scale = 1.0f / std::sqrt(static_cast<float>(d));
+  P.q = Tensor{q, st[0].sb, st[0].sh, st[0].sn};
+  P.k = Tensor{k, st[1].sb, st[1].sh, st[1].sn};
+  P.v = Tensor{v, st[2].sb, st[2].sh, st[2].sn};
+  P.o = Tensor{out, st[3].sb, st[3].sh, st[3].sn};
+  P.qbar = reinterpret_cast<float*>(ws + L.qbar);
+  P.kbar = reinterpret_cast<float*>(ws + L.kbar);
+  P.vbar = reinterpret_cast<float*>(ws + L.vbar);
+  P.scores = reinterpret_cast<float*>(ws + L.scores);
+  P.kept_cnt = reinterpret_cast<int*>(ws + L.kept_cnt);
+  P.kept_idx = reinterpret_cast<int*>(ws + L.kept_idx);
+  P.mult = reinterpret_cast<uint8_t*>(ws + L.mult);
+  P.extra_cnt = reinterpret_cast<int*>(ws + L.extra_cnt);
+  P.extra_idx = reinterpret_cast<int*>(ws + L.extra_idx);
+  P.extra_buf = reinterpret_cast<uint2*>(ws + L.extra_buf);
+  if (dtype == SOLATTN_BF16) {
+    P.kbar_bf = reinterpret_cast<uint16_t*>(ws + L.kbar_bf);
+    P.vbar_t = reinterpret_cast<uint16_t*>(ws + L.vbar_t);
+    P.v_t = reinterpret_cast<uint16_t*>(ws + L.v_t);
+  }
+
+  std::unique_lock<std::mutex> tl(g_t_mu);
+  const bool timing = g_timing;
+  TimedCall tc;
+  std::memset(&tc, 0, sizeof tc);
+  if (timing) {
+    for (int e = 0; e <= NK; ++e) {
+      tc.ev[e] = take_event();
+      if (!tc.ev[e]) return fail(SOLATTN_EHIP, "hipEventCreate");
+    }
+  } else {
+    tl.unlock();
+  }
+  auto mark = [&](int e) {
+    if (timing) hipEventRecord(tc.ev[e], stream);
+  };
+
+  const bool do_extra = extra_tokens > 0 && !P.keep_all;
+  hipError_t err;
+  mark(0);
+  if ((err = solattn::launch_block_pool(P, stream)) != hipSuccess)
+    return fail(SOLATTN_EHIP, "block_pool: %s", hipGetErrorString(err));
+  tc.ran[0] = true;
+  mark(1);
+  if ((err = solattn::launch_block_score(P, stream)) != hipSuccess)
+    return fail(SOLATTN_EHIP, "block_score: %s", hipGetErrorString(err));
+  tc.ran[1] = true;
+  mark(2);
+  if ((err = solattn::launch_block_select(P, stream)) != hipSuccess)
+    return fail(SOLATTN_EHIP, "block_select: %s", hipGetErrorString(err));
+  tc.ran[2] = true;
+  mark(3);
+  if (do_extra) {
+    if ((err = solattn::launch_extra_select(P, stream)) != hipSuccess)
+      return fail(SOLATTN_EHIP, "extra_select: %s", hipGetErrorString(err));
+    tc.ran[3] = true;
+  }
+  mark(4);
+  if ((err = solattn::launch_sparse_flash(P, stream)) != hipSuccess)
+    return fail(SOLATTN_EHIP, "sparse_flash_fwd: %s", hipGetErrorString(err));
+  tc.ran[4] = true;
+  mark(5);
+  if (timing) g_calls.push_back(tc);
+  return SOLATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sol_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d, float tau,
+                 int block_q, int block_k, int sink_range, int extra_tokens, const solattn_opts* opts) {
+  return run(SOLATTN_MODE_SOL, q, k, v, out, B, H, N, d, tau, 100.f, block_q, block_k, sink_range,
+             extra_tokens, opts);
+}
+
+int sla_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d, int block_q,
+                 int block_k, int sink_range, int extra_tokens, float keep_percent, const solattn_opts* opts) {
+  return run(SOLATTN_MODE_SLA, q, k, v, out, B, H, N, d, 0.f, keep_percent, block_q, block_k, sink_range,
+             extra_tokens, opts);
+}
+
+int solattn_check_args(int mode, const void* q, const void* k, const void* v, void* out, int B, int H, int N,
+                       int d, float tau, float keep_percent, int block_q, int block_k, int sink_range,
+                       int extra_tokens, const solattn_opts* opts) {
+  g_err.clear();
+  Strides st[4];
+  return check(mode, q, k, v, out, B, H, N, d, tau, keep_percent, block_q, block_k, sink_range, extra_tokens,
+               opts, st);
+}
+
+int solattn_workspace_layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k,
+                             solattn_ws_layout* out) {
+  if (!out) return SOLATTN_EINVAL;
+  return layout(mode, dtype, B, H, N, d, block_q, block_k, out);
+}
+
+size_t solattn_workspace_bytes(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k) {
+  solattn_ws_layout L;
+  if (layout(mode, dtype, B, H, N, d, block_q, block_k, &L) != SOLATTN_OK) return 0;
+  return L.total;
+}
+
+const char* solattn_status_string(int status) {
+  switch (status) {
+    case SOLATTN_OK: return "ok";
+    case SOLATTN_EINVAL: return "invalid argument";
+    case SOLATTN_ENOTSUP: return "not supported by this build";
+    case SOLATTN_EWORKSPACE: return "workspace too small";
+    case SOLATTN_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* solattn_last_error(void) { return g_err.c_str(); }
+
+int solattn_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_t_mu);
+  g_timing = enable != 0;
+  return SOLATTN_OK;
+}
+
+int solattn_timing_read(double* ms, long long* launches, int n) {
+  std::lock_guard<std::mutex> lk(g_t_mu);
+  if (n < 0 || (n > 0 && (!ms || !launches))) return SOLATTN_EINVAL;
+  for (int i = 0; i < n; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  int rc = SOLATTN_OK;
+  for (TimedCall& c : g_calls) {
+    if (hipEventSynchronize(c.ev[NK]) != hipSuccess) rc = SOLATTN_EHIP;
+    for (int kx = 0; kx < NK && kx < n; ++kx) {
+      if (!c.ran[kx]) continue;
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, c.ev[kx], c.ev[kx + 1]) != hipSuccess) rc = SOLATTN_EHIP;
+      ms[kx] += t;
+      launches[kx] += 1;
+    }
+    for (int e = 0; e <= NK; ++e) g_free_events.push_back(c.ev[e]);
+  }
+  g_calls.clear();
+  return rc;
+}
+
+const char* solattn_kernel_name(int index) {
+  if (index < 0 || index >= NK) return "";
+  return kKernelNames[index];
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Shared definitions of the libsolattn kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace solattn {
+
+// A strided [B, H, N, d] tensor: element strides of the b, h and n axes; d is contiguous.
+struct Tensor {
+  const void* p;
+  int64_t sb, sh, sn;
+};
+
+// Everything one call's kernels need, passed by value to each launch.
+struct Problem {
+  int B, H, N, d;
+  int bq, bk;            // query / key block sizes
+  int Mq, M, Mpad;       // query blocks, key blocks, key blocks rounded up to 64
+  int mode;              // 0 sol, 1 sla
+  int dtype;             // 0 bf16, 1 fp32
+  float tau;
+  int keep_all;          // tau == -inf: every block kept
+  int k_sla;             // sla: ceil(keep_percent * M / 100)
+  int sink_blocks;       // key blocks overlapping [0, sink_range)
+  int extra;             // extra tokens per query block (0..256)
+  int dense_q0, dense_q1;  // query blocks [dense_q0, dense_q1) attend every key
+  float scale;           // 1/sqrt(d)
+  Tensor q, k, v, o;
+  // workspace
+  float* qbar;
+  float* kbar;
+  float* vbar;
+  float* scores;
+  int* kept_cnt;
+  int* kept_idx;
+  uint8_t* mult;
+  int* extra_cnt;
+  int* extra_idx;
+  uint2* extra_buf;      // per query block: (score bits, token) candidate buffer, EXTRA_CAP entries
+  uint16_t* kbar_bf;
+  uint16_t* vbar_t;
+  uint16_t* v_t;
+};
+
+constexpr int MAX_EXTRA = 256;
+constexpr int EXTRA_SLACK = 128;                 // candidates one token chunk can add per row
+constexpr int EXTRA_CAP = MAX_EXTRA + EXTRA_SLACK;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key); -0 maps like +0.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Position of key `kk` (0..63) inside a 64-key transposed V tile.  Inside each group of 16 keys
+// bits 2 and 3 of the index are swapped, so that the 8 keys one lane feeds to the PV matrix
+// instruction (given the 32x32 accumulator layout of the score tile) sit next to each other.
+__host__ __device__ __forceinline__ int vt_pos(int kk) {
+  return (kk & ~0xC) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+}
+
+}  // namespace solattn

@@ -1,0 +1,173 @@
+// block_select: per (head, query block) row of block scores, choose the key blocks attended
+// exactly and compact them into an ascending index list.
+//   sol-attn (node docs, sol-attn table, tau row): keep s_ij > mean + tau*std of the row,
+//     std the population deviation over all M blocks (two passes).
+//   sla (node docs, sla table, keep_percent row): keep the k highest non-forced blocks,
+//     ties to the lower index (radix select on order-preserving keys).
+//   Sink blocks and the diagonal block(s) are kept on top in both modes (node docs, sla
+//   table, and sink_conditioning row).  Query blocks in the dense row range keep every block.
+// One 256-thread workgroup per row; all reductions have a fixed order, so results are
+// deterministic.  Also writes each block's centroid multiplicity (0 = attended exactly).
+#include "common.h"
+#include "launch.h"
+
+namespace solattn {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Sum over the 256 threads, identical result on every thread.
+__device__ float block_sum(float v, float* sh) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / 64;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  return ((sh[0] + sh[1]) + sh[2]) + sh[3];
+}
+
+// Inclusive prefix sum over the 256 threads (thread order).  *total gets the sum.
+__device__ int block_scan_incl(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x / 64;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  __syncthreads();
+  if (lane == 63) sh[w] = v;
+  __syncthreads();
+  int before = 0;
+  for (int u = 0; u < w; ++u) before += sh[u];
+  *total = sh[0] + sh[1] + sh[2] + sh[3];
+  return v + before;
+}
+
+__global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
+  __shared__ float fsh[4];
+  __shared__ int ish[4];
+  __shared__ int hist[256];
+  __shared__ int pick[2];
+
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int M = P.M;
+  const size_t row = (size_t)bh * P.Mq + i;
+  const float* s = P.scores + row * M;
+  int* kidx = P.kept_idx + row * M;
+  uint8_t* mult = P.mult + row * P.Mpad;
+
+  const bool dense = i >= P.dense_q0 && i < P.dense_q1;
+  if (dense || (P.mode == 0 && P.keep_all)) {
+    for (int j = tid; j < P.Mpad; j += 256) {
+      if (j < M) kidx[j] = j;
+      mult[j] = 0;
+    }
+    if (tid == 0) {
+      P.kept_cnt[row] = M;
+      P.extra_cnt[row] = 0;
+    }
+    return;
+  }
+
+  // forced blocks: the sinks and every key block overlapping this query block's tokens
+  const int diag_lo = (i * P.bq) / P.bk;
+  const int diag_hi = min(M - 1, ((i + 1) * P.bq - 1) / P.bk);
+  auto forced = [&](int j) { return j < P.sink_blocks || (j >= diag_lo && j <= diag_hi); };
+
+  float theta = 0.f;          // sol threshold
+  uint32_t kstar = 0;         // sla: key of the k-th largest non-forced score
+  int need_eq = 0;            // sla: how many scores equal to kstar to take (lowest index first)
+  bool sla_any = false;
+
+  if (P.mode == 0) {
+    float acc = 0.f;
+    for (int j = tid; j < M; j += 256) acc += s[j];
+    const float mu = block_sum(acc, fsh) / static_cast<float>(M);
+    float acc2 = 0.f;
+    for (int j = tid; j < M; j += 256) {
+      const float dv = s[j] - mu;
+      acc2 = fmaf(dv, dv, acc2);
+    }
+    const float var = block_sum(acc2, fsh) / static_cast<float>(M);
+    const float sd = sqrtf(var);
+    theta = sd > 0.f ? fmaf(P.tau, sd, mu) : mu;
+  } else {
+    const int nforced = min(P.sink_blocks, M) + (diag_hi - diag_lo + 1) -
+                        max(0, min(diag_hi, P.sink_blocks - 1) - diag_lo + 1);
+    int need = min(M - nforced, P.k_sla);
+    sla_any = need > 0;
+    if (sla_any) {
+      uint32_t prefix = 0, pmask = 0;
+      for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        hist[tid] = 0;
+        __syncthreads();
+        for (int j = tid; j < M; j += 256) {
+          if (forced(j)) continue;
+          const uint32_t key = float_key(s[j]);
+          if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        // thread t looks at digit 255-t; counts accumulate from the top digit down
+        const int c = hist[255 - tid];
+        int total;
+        const int incl = block_scan_incl(c, ish, &total);
+        const int excl = incl - c;
+        if (excl < need && need <= incl) {
+          pick[0] = 255 - tid;
+          pick[1] = excl;
+        }
+        __syncthreads();
+        prefix |= static_cast<uint32_t>(pick[0]) << shift;
+        pmask |= 0xFFu << shift;
+        need -= pick[1];
+        __syncthreads();
+      }
+      kstar = prefix;
+      need_eq = need;
+    }
+  }
+
+  // ordered compaction of the kept blocks
+  int base = 0, eq_base = 0;
+  for (int j0 = 0; j0 < M; j0 += 256) {
+    const int j = j0 + tid;
+    bool keep = false, eq = false;
+    if (j < M) {
+      if (forced(j)) {
+        keep = true;
+      } else if (P.mode == 0) {
+        keep = s[j] > theta;
+      } else if (sla_any) {
+        const uint32_t key = float_key(s[j]);
+        keep = key > kstar;
+        eq = key == kstar;
+      }
+    }
+    int tot_eq;
+    const int eq_rank = block_scan_incl(eq ? 1 : 0, ish, &tot_eq) - (eq ? 1 : 0) + eq_base;
+    if (eq && eq_rank < need_eq) keep = true;
+    eq_base += tot_eq;
+    int tot;
+    const int pos = block_scan_incl(keep ? 1 : 0, ish, &tot) - (keep ? 1 : 0) + base;
+    if (keep) kidx[pos] = j;
+    if (j < M) mult[j] = keep ? 0 : static_cast<uint8_t>(P.bk);
+    base += tot;
+  }
+  for (int j = M + tid; j < P.Mpad; j += 256) mult[j] = 0;
+  if (tid == 0) {
+    P.kept_cnt[row] = base;
+    P.extra_cnt[row] = 0;
+  }
+}
+
+hipError_t launch_block_select(const Problem& P, hipStream_t stream) {
+  dim3 grid(P.Mq, P.B * P.H);
+  hipLaunchKernelGGL(block_select_kernel, grid, dim3(256), 0, stream, P);
+  return hipGetLastError();
+}
+
+}  // namespace solattn

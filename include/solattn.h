@@ -1,0 +1,172 @@
+/*
+ * libsolattn: block-sparse attention forward (sol-attn and sla) for AMD gfx950.
+ *
+ * The operation (ComfyUI "BlockSparseAttention" node docs, input tables; the
+ * minimax-h3-chunk-star7 README, sections "Sol" and "SLA"), per (batch, head):
+ *   1. mean-pool Q over block_q tokens and K, V over block_k tokens;
+ *   2. score every pooled query block against every pooled key block,
+ *      s_ij = q̄_i . k̄_j / sqrt(d);
+ *   3. select key blocks per query block: sol-attn keeps s_ij > mean + tau*std
+ *      of the row (node docs, sol-attn table, tau row); sla keeps the
+ *      ceil(keep_percent*M/100) highest (node docs, sla table, keep_percent
+ *      row).  Sink blocks (overlapping [0, sink_range): the packed conditioning
+ *      rows, node docs, sink_conditioning row) and the diagonal blocks are kept
+ *      on top;
+ *   4. add up to extra_tokens individually highest-scoring keys (q̄_i . k_t)
+ *      outside the kept blocks (node docs, extra_tokens row);
+ *   5. attend exactly over kept-block and extra tokens; for sol-attn every other
+ *      key block enters through its centroid (k̄_j, v̄_j) with weight
+ *      (tokens of the block not attended exactly) in the same FP32 online
+ *      softmax (star7 README, "Sol"); sla drops them (star7 README, "SLA").
+ *   Query rows in [dense_row_begin, dense_row_end) attend every key exactly
+ *   (node docs, sink_conditioning row: exact_kv_and_rows).
+ * Attention is non-causal with scale 1/sqrt(d).
+ *
+ * All calls are asynchronous on the given HIP stream: a return of SOLATTN_OK
+ * means the work was enqueued.  Every argument is validated on the host before
+ * anything is launched, so an error return never leaves a partial write.
+ */
+#ifndef SOLATTN_H
+#define SOLATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SOLATTN_OK          0
+#define SOLATTN_EINVAL     -1   /* an argument is out of its domain                        */
+#define SOLATTN_ENOTSUP    -2   /* valid, but this build does not implement the shape      */
+#define SOLATTN_EWORKSPACE -3   /* the caller's workspace is smaller than required        */
+#define SOLATTN_EHIP       -4   /* a HIP runtime or launch error (detail in last_error)    */
+
+/* Element types of q, k, v and out (all four share one type). */
+#define SOLATTN_BF16 0
+#define SOLATTN_FP32 1
+
+/* Selection modes. */
+#define SOLATTN_MODE_SOL 0
+#define SOLATTN_MODE_SLA 1
+
+/* Largest extra_tokens value (node docs, extra_tokens row: 0..256). */
+#define SOLATTN_MAX_EXTRA 256
+
+/*
+ * Optional per-call settings.  Pass NULL for the defaults: bf16, contiguous
+ * [B, H, N, d] tensors, no dense rows, the null stream, a library-owned
+ * workspace.  Set struct_size = sizeof(solattn_opts) and zero every field you
+ * do not use.
+ */
+typedef struct solattn_opts {
+  int struct_size;
+  int dtype;                      /* SOLATTN_BF16 or SOLATTN_FP32                          */
+  /* Strides in elements of the b, h and n axes; the d axis is contiguous.  A
+   * triple of zeros means contiguous [B, H, N, d].  Row starts (every n) must
+   * be 16-byte aligned. */
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+  int dense_row_begin, dense_row_end;   /* query rows attending every key; empty if equal */
+  void*  workspace;               /* device buffer owned by the caller, or NULL            */
+  size_t workspace_bytes;         /* its size; must be >= solattn_workspace_bytes(...)     */
+  void*  stream;                  /* hipStream_t; NULL = null stream                       */
+} solattn_opts;
+
+/*
+ * sol-attn forward.
+ *   q, k, v   device pointers, read only, layout given by opts (default [B,H,N,d]).
+ *   out       device pointer, same shape and type, fully overwritten; must not
+ *             overlap q, k or v.
+ *   B, H, N, d  sizes (>= 1).  This build: d in {64, 128}, N % block_q == 0,
+ *             N % block_k == 0.
+ *   tau       threshold in standard deviations of the row's block scores; any
+ *             value but NaN.  -inf keeps every block (dense attention).
+ *   block_q   query block size: 64 or 128.   block_k: key block size: 64.
+ *   sink_range  0..N; every key block overlapping tokens [0, sink_range) is
+ *             attended exactly by every query (0 = none).
+ *   extra_tokens  0..256 extra exact keys per query block.
+ * Returns a status code.
+ */
+int sol_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                 int B, int H, int N, int d, float tau,
+                 int block_q, int block_k, int sink_range, int extra_tokens,
+                 const solattn_opts* opts);
+
+/*
+ * sla forward: as sol_attn_fwd, but step 3 keeps the ceil(keep_percent*M/100)
+ * highest-scoring non-forced key blocks (ties to the lower block index) and
+ * skipped blocks contribute nothing.  keep_percent in (0, 100].
+ */
+int sla_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                 int B, int H, int N, int d,
+                 int block_q, int block_k, int sink_range, int extra_tokens, float keep_percent,
+                 const solattn_opts* opts);
+
+/*
+ * Host-only argument check: the exact validation the two calls above perform,
+ * without launching anything.  mode is SOLATTN_MODE_SOL or SOLATTN_MODE_SLA
+ * (keep_percent is ignored for sol, tau for sla).  Returns a status code.
+ */
+int solattn_check_args(int mode, const void* q, const void* k, const void* v, void* out,
+                       int B, int H, int N, int d, float tau, float keep_percent,
+                       int block_q, int block_k, int sink_range, int extra_tokens,
+                       const solattn_opts* opts);
+
+/*
+ * Workspace.  Byte offsets (from the workspace start, each 256-byte aligned) of
+ * the intermediate buffers of one call, which stay readable after the call
+ * until the workspace is reused:
+ *   qbar      fp32 [B*H, Mq, d]    pooled queries
+ *   kbar      fp32 [B*H, M, d]     pooled keys
+ *   vbar      fp32 [B*H, M, d]     pooled values
+ *   scores    fp32 [B*H, Mq, M]    block scores s_ij
+ *   kept_cnt  int32 [B*H, Mq]      number of kept key blocks (M for dense query blocks)
+ *   kept_idx  int32 [B*H, Mq, M]   kept key-block indices, ascending, first kept_cnt valid
+ *   mult      uint8 [B*H, Mq, Mpad] centroid multiplicity of each key block (0 = attended exactly)
+ *   extra_cnt int32 [B*H, Mq]      number of extra tokens
+ *   extra_idx int32 [B*H, Mq, 256] extra token indices, ascending, first extra_cnt valid
+ *   extra_buf 8-byte entries [B*H, Mq, 384]: scratch of the extra-token selection
+ *   kbar_bf   bf16 [B*H, Mpad, d], vbar_t bf16 [B*H, Mpad/64, d, 64], v_t bf16
+ *             [B*H, M, d, 64]: operand copies for the attention kernel (bf16 only)
+ * Mq = N/block_q, M = N/block_k, Mpad = M rounded up to a multiple of 64.
+ */
+typedef struct solattn_ws_layout {
+  size_t total;
+  size_t qbar, kbar, vbar, scores, kept_cnt, kept_idx, mult, extra_cnt, extra_idx;
+  size_t extra_buf;             /* candidate buffers of the extra-token selection          */
+  size_t kbar_bf, vbar_t, v_t;
+  int Mq, M, Mpad;
+} solattn_ws_layout;
+
+/* Fills *layout for a call of this shape.  Returns SOLATTN_OK or SOLATTN_EINVAL. */
+int solattn_workspace_layout(int mode, int dtype, int B, int H, int N, int d,
+                             int block_q, int block_k, solattn_ws_layout* layout);
+
+/* Total workspace bytes for a call of this shape (0 if the shape is invalid). */
+size_t solattn_workspace_bytes(int mode, int dtype, int B, int H, int N, int d,
+                               int block_q, int block_k);
+
+/* Static text for a status code. */
+const char* solattn_status_string(int status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* solattn_last_error(void);
+
+/*
+ * Per-kernel timing.  While enabled, every call records HIP events around each
+ * of its kernel launches on the call's stream.  solattn_timing_read waits for
+ * those events, writes the summed milliseconds and launch counts per kernel
+ * (index order: block_pool, block_score, block_select, extra_select,
+ * sparse_flash_fwd) into ms[0..n) and launches[0..n), and resets the sums.
+ */
+#define SOLATTN_NKERNELS 5
+int solattn_timing_enable(int enable);
+int solattn_timing_read(double* ms, long long* launches, int n);
+const char* solattn_kernel_name(int index);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOLATTN_H */

@@ -1,0 +1,115 @@
+"""The C ABI on the host: the library loads, exports every symbol include/solattn.h declares,
+and validates arguments before any launch (no GPU needed: every call here fails validation or
+only plans the workspace)."""
+import ctypes
+import json
+import math
+import os
+
+import pytest
+
+import block_sparse_attention_scores_amd as sa
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
+
+# fake, non-overlapping, 256-aligned "device" addresses: never dereferenced
+QP, KP, VP, OP = 1 << 32, 2 << 32, 3 << 32, 4 << 32
+
+
+def check(mode=0, q=QP, k=KP, v=VP, o=OP, B=1, H=2, N=4096, d=64, tau=1.3, keep=10.0, bq=64, bk=64,
+          sink=0, extra=0, opts=None):
+    return sa.lib().solattn_check_args(mode, q, k, v, o, B, H, N, d, tau, keep, bq, bk, sink, extra,
+                                       ctypes.byref(opts) if opts is not None else None)
+
+
+def test_exports_every_declared_symbol():
+    L = sa.lib()
+    names = sa.header_functions()
+    assert {"sol_attn_fwd", "sla_attn_fwd", "solattn_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_valid_arguments_pass():
+    assert check() == sa.OK
+    assert check(mode=1, bq=128, keep=15.0) == sa.OK
+    assert check(d=128, extra=256, sink=1024, tau=-math.inf) == sa.OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(o=0), dict(B=0), dict(H=0), dict(N=0), dict(d=0),
+    dict(tau=float("nan")), dict(mode=1, keep=0.0), dict(mode=1, keep=100.5),
+    dict(mode=1, keep=float("nan")), dict(extra=-1), dict(extra=257), dict(sink=-1),
+    dict(sink=4097), dict(mode=7), dict(bq=0), dict(o=QP + 64),
+])
+def test_invalid_arguments(kw):
+    assert check(**kw) == sa.EINVAL
+    assert sa.last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [
+    dict(d=96), dict(bk=32), dict(bq=32), dict(N=4000), dict(q=QP + 8),
+])
+def test_unsupported_shapes(kw):
+    assert check(**kw) == sa.ENOTSUP
+
+
+def test_dense_row_and_stride_validation():
+    o = sa.make_opts(dense_rows=(4096 - 1024, 4096))
+    assert check(opts=o) == sa.OK
+    assert check(opts=sa.make_opts(dense_rows=(100, 50))) == sa.EINVAL
+    assert check(opts=sa.make_opts(dense_rows=(0, 5000))) == sa.EINVAL
+    assert check(opts=sa.make_opts(dense_rows=(32, 4096))) == sa.ENOTSUP
+    bad = sa.make_opts()
+    bad.struct_size = 8
+    assert check(opts=bad) == sa.EINVAL
+    assert check(opts=sa.make_opts(dtype=5)) == sa.EINVAL
+    # out rows overlapping each other
+    st = [(0, 0, 0)] * 3 + [(2 * 4096 * 64, 4096 * 64, 32)]
+    assert check(opts=sa.make_opts(strides=st)) == sa.EINVAL
+    # a strided q view ([B, N, H, d] memory) is fine
+    st = [(4096 * 2 * 64, 64, 2 * 64)] + [(0, 0, 0)] * 3
+    assert check(opts=sa.make_opts(strides=st)) == sa.OK
+
+
+def test_forward_calls_fail_before_launching():
+    L = sa.lib()
+    rc = L.sol_attn_fwd(QP, KP, VP, QP, 1, 2, 4096, 64, 1.3, 64, 64, 0, 0, None)
+    assert rc == sa.EINVAL and "overlaps" in sa.last_error()
+    rc = L.sla_attn_fwd(QP, KP, VP, OP, 1, 2, 4096, 64, 128, 64, 0, 0, -3.0, None)
+    assert rc == sa.EINVAL and "keep_percent" in sa.last_error()
+
+
+def test_page_parameter_ranges_are_accepted():
+    g = json.load(open(GOLDEN))
+    assert check(extra=g["extra_tokens_range"]["max"]) == sa.OK
+    assert check(extra=g["extra_tokens_range"]["max"] + 1) == sa.EINVAL
+    assert check(mode=1, bq=128, keep=g["keep_percent_range"]["min"]) == sa.OK
+    assert check(mode=1, bq=128, keep=g["keep_percent_range"]["max"]) == sa.OK
+    for t in (g["tau_range"]["min"], g["tau_range"]["max"], g["tau_range"]["default"]):
+        assert check(tau=t) == sa.OK
+    bq, bk = g["block_sizes"]["sla"]
+    assert check(mode=1, bq=bq, bk=bk) == sa.OK
+
+
+def test_workspace_layout():
+    L = sa.workspace_layout(sa.MODE_SOL, sa.BF16, 1, 24, 65536, 128, 64, 64)
+    assert (L.Mq, L.M, L.Mpad) == (1024, 1024, 1024)
+    offs = [L.qbar, L.kbar, L.vbar, L.scores, L.kept_cnt, L.kept_idx, L.mult, L.extra_cnt,
+            L.extra_idx, L.extra_buf, L.kbar_bf, L.vbar_t, L.v_t]
+    assert all(o % 256 == 0 for o in offs)
+    assert offs == sorted(offs) and L.total > L.v_t
+    assert L.scores - L.vbar >= 24 * 1024 * 128 * 4
+    a = sa.workspace_bytes(0, 0, 1, 24, 16384, 128, 64, 64)
+    b = sa.workspace_bytes(0, 0, 1, 24, 32768, 128, 64, 64)
+    assert 0 < a < b
+    assert sa.workspace_bytes(0, 0, 0, 24, 16384, 128, 64, 64) == 0
+    Lf = sa.workspace_layout(sa.MODE_SLA, sa.FP32, 1, 2, 4096, 64, 128, 64)
+    assert Lf.Mpad == 64 and Lf.v_t == 0
+
+
+def test_status_strings_and_kernel_names():
+    assert sa.status_string(0) == "ok"
+    assert "workspace" in sa.status_string(sa.EWORKSPACE)
+    assert sa.kernel_names() == ["block_pool", "block_score", "block_select", "extra_select",
+                                 "sparse_flash_fwd"]

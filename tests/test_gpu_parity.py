@@ -1,0 +1,165 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on seeded inputs.
+
+Small cases are compared element by element on every output row; the full-size workloads
+(N = 65536 and N = 202752, all 24 heads, the launch the bench times) are checked on every
+intermediate of sampled heads and on the outputs of sampled query blocks.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_scores_amd as sa
+from gen import make_inputs, random_qkv, workload
+from oracle import dense, solattn
+from parity import Report, check_head, device_inputs, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def params(w, **ov):
+    p = dict(block_q=w.block_q, block_k=w.block_k, tau=w.tau, keep_percent=w.keep_percent,
+             sink_range=w.sink_range, extra_tokens=w.extra_tokens, dense_rows=w.dense_rows)
+    p.update(ov)
+    return p
+
+
+def run_and_check(w, x, heads_to_check, qblocks=None, mode=None, **ov):
+    mode = mode or w.mode
+    p = params(w, **ov)
+    print(f"\n[parity] {w.name} mode={mode} H={x.q.shape[1]} N={w.N} {p}", flush=True)
+    q, k, v = device_inputs(x)
+    out, sel = run_gpu(mode, q, k, v, **p)
+    rep = Report()
+    for h in heads_to_check:
+        xin = (x.q[0, h].astype(np.float64), x.k[0, h].astype(np.float64), x.v[0, h].astype(np.float64))
+        ref = solattn.head_forward(mode, *xin, **p, want_out=False)
+        qb = qblocks(h, ref) if callable(qblocks) else qblocks
+        check_head(mode, ref, sel, h, x_in=xin, d=w.d, N=w.N, report=rep, qblocks=qb,
+                   out_gpu=out[0, h], dtype=x.w.dtype, **p)
+    print(f"[parity] rows={rep.rows} mask_flips={rep.mask_flips} extra_flips={rep.extra_flips} "
+          f"max_abs={rep.max_abs:.3e} mean_abs={rep.mean_abs:.3e}", flush=True)
+    return out, sel, rep
+
+
+def test_tiny_sol_fp32():
+    w = workload(1)
+    x = make_inputs(w)
+    run_and_check(w, x, range(w.H))
+
+
+@pytest.mark.parametrize("tau", [1.0, 1.3, 2.0])
+def test_sol_bf16_n16k_tau_sweep(tau):
+    w = workload(2, tau=tau)
+    x = make_inputs(w, heads=[0, 7, 19])
+    run_and_check(w, x, range(3))
+
+
+def test_sla_bf16_n32k():
+    w = workload(3)
+    x = make_inputs(w, heads=[0, 11])
+    run_and_check(w, x, range(2))
+
+
+@pytest.mark.parametrize("extra", [64, 192])
+def test_sol_bf16_extra_partial_tiles(extra):
+    w = workload(2, extra_tokens=extra, dense_rows=(16384 - 1024, 16384))
+    x = make_inputs(w, heads=[3])
+    run_and_check(w, x, range(1))
+
+
+def _sample(rng_seed, n_sparse=6, n_dense=2):
+    def pick(h, ref):
+        rng = np.random.default_rng(rng_seed + h)
+        sparse = np.flatnonzero(~ref["dense"])
+        dn = np.flatnonzero(ref["dense"])
+        out = list(rng.choice(sparse, size=min(n_sparse, sparse.size), replace=False))
+        if dn.size:
+            out += list(rng.choice(dn, size=min(n_dense, dn.size), replace=False))
+        return sorted(int(i) for i in out)
+    return pick
+
+
+def test_sol_full_options_n64k_all_heads():
+    w = workload(4)
+    x = make_inputs(w)
+    run_and_check(w, x, [0, 13, 23], qblocks=_sample(40))
+
+
+def test_sol_long_n203k_all_heads():
+    w = workload(5)
+    x = make_inputs(w)
+    run_and_check(w, x, [5], qblocks=_sample(50, n_sparse=4))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("case", ["tau_neg_inf", "sla_all", "sink_all"])
+def test_dense_limits(dtype, case):
+    x = random_qkv(1, 2, 2048, 64, seed=5, dtype=dtype)
+    q, k, v = device_inputs(x)
+    if case == "tau_neg_inf":
+        out, sel = run_gpu("sol", q, k, v, block_q=64, block_k=64, tau=-math.inf, extra_tokens=128)
+    elif case == "sla_all":
+        out, sel = run_gpu("sla", q, k, v, block_q=128, block_k=64, keep_percent=100.0)
+    else:
+        out, sel = run_gpu("sol", q, k, v, block_q=64, block_k=64, tau=1.3, sink_range=2048,
+                           extra_tokens=64)
+    ref = np.stack([dense.dense_attention(x.q[0, h], x.k[0, h], x.v[0, h]) for h in range(2)])
+    err = np.abs(out[0] - ref)
+    tol = (2e-2, 2e-3) if dtype == "bf16" else (1e-4, 1e-4)
+    assert err.max() <= tol[0] and err.mean() <= tol[1], (err.max(), err.mean())
+
+
+def test_few_candidates_for_extra_tokens():
+    # tau = -2 keeps almost every block: fewer candidate tokens than extra_tokens
+    w = workload(1, dtype="bf16", d=128, H=2, tau=-2.0, extra_tokens=256)
+    x = make_inputs(w)
+    _, sel, _ = run_and_check(w, x, range(2))
+    assert (sel["extra_cnt"] < 256).any()
+
+
+def test_batch_and_dense_rows_fp32():
+    x = random_qkv(2, 2, 4096, 64, seed=9, dtype="fp32")
+    w = workload(1, B=2, dense_rows=(3072, 4096), extra_tokens=64, sink_range=100)
+    x.w = w
+    q, k, v = device_inputs(x)
+    p = params(w)
+    out, sel = run_gpu("sol", q, k, v, **p)
+    for b in range(2):
+        for h in range(2):
+            xin = (x.q[b, h].astype(np.float64), x.k[b, h].astype(np.float64), x.v[b, h].astype(np.float64))
+            ref = solattn.head_forward("sol", *xin, **p, want_out=False)
+            sub = {k_: v_[b * 2 + h:b * 2 + h + 1] for k_, v_ in sel.items()}
+            check_head("sol", ref, sub, 0, x_in=xin, d=64, N=4096, report=Report(),
+                       out_gpu=out[b, h], dtype="fp32", **p)
+
+
+def test_deterministic_and_strided_views():
+    w = workload(2, H=2, extra_tokens=128, dense_rows=(15360, 16384))
+    x = make_inputs(w)
+    q, k, v = device_inputs(x)
+    p = params(w)
+    o1, _ = run_gpu("sol", q, k, v, **p)
+    o2, _ = run_gpu("sol", q, k, v, **p)
+    assert np.array_equal(o1, o2)
+    # the same tensors as views of a [B, N, H, d] buffer
+    qs, ks, vs = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v))
+    assert not qs.is_contiguous()
+    o3, _ = run_gpu("sol", qs, ks, vs, **p)
+    assert np.array_equal(o1, o3)
+
+
+def test_library_errors_raise():
+    x = random_qkv(1, 1, 4096, 64, seed=1, dtype="bf16")
+    q, k, v = device_inputs(x)
+    with pytest.raises(sa.SolattnError) as e:
+        sa.sol_attn(q, k, v, tau=float("nan"))
+    assert e.value.status == sa.EINVAL
+    with pytest.raises(sa.SolattnError) as e:
+        sa.sol_attn(q, k, v, block_k=32)
+    assert e.value.status == sa.ENOTSUP
+    ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sa.SolattnError) as e:
+        sa.sol_attn(q, k, v, workspace=ws)
+    assert e.value.status == sa.EWORKSPACE
