@@ -1,0 +1,261 @@
+"""Benchmark of the sol-attn / sla forward on one MI355X.
+
+Default workload: sol-attn with every option on, B=1, H=24, N=65536 (16 x 64 x 64 latent grid),
+d=128, bf16, Q64/K64 blocks, tau=1.3, extra_tokens=256, 1024-token exact sink, last 2048 query rows
+dense.  Inputs are seeded synthetic video-like latents (see gen/inputs.py) resident in HBM
+before timing starts.  One step = one whole forward call (pool, score, select, extra tokens,
+attention).  Prints one JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 matrix peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, help="workload id (gen/inputs.py)")
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def selection_stats(sel, w, B, H):
+    """Exact (row, key) pairs and centroid terms of the run's actual selection."""
+    kept = sel["kept_cnt"].astype(np.int64)          # [BH, Mq]
+    extra = sel["extra_cnt"].astype(np.int64)
+    Mq, M = kept.shape[1], w.N // w.block_k
+    dq0, dq1 = w.dense_rows[0] // w.block_q, w.dense_rows[1] // w.block_q
+    dense = np.zeros(Mq, dtype=bool)
+    dense[dq0:dq1] = True
+    exact_keys = kept * w.block_k + np.where(dense[None, :], 0, extra)
+    exact_pairs = int((exact_keys * w.block_q).sum())
+    cent = 0
+    if w.mode == "sol":
+        m = sel["mult"][:, :, :M]
+        cent = int(((m > 0).sum(axis=2) * w.block_q).sum())
+    sparse_rows = ~dense
+    kept_frac = float(kept[:, sparse_rows].sum()) / float(B * H * sparse_rows.sum() * M) \
+        if sparse_rows.any() else 1.0
+    return exact_pairs, cent, kept_frac
+
+
+def cpu_baseline(w, x, heads=(0,), n_sparse=24, n_dense=4, seed=7):
+    """Time the oracle on a bounded sample and extrapolate to one whole call."""
+    from oracle import solattn
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    p = dict(block_q=w.block_q, block_k=w.block_k, tau=w.tau, keep_percent=w.keep_percent,
+             sink_range=w.sink_range, extra_tokens=w.extra_tokens, dense_rows=w.dense_rows)
+    t_sel = []
+    t_sparse, t_dense = [], []
+    rng = np.random.default_rng(seed)
+    for h in heads:
+        xin = [a[0, h].astype(np.float64) for a in (x.q, x.k, x.v)]
+        t0 = time.perf_counter()
+        ref = solattn.head_forward(w.mode, *xin, **p, want_out=False)
+        t_sel.append(time.perf_counter() - t0)
+        sel = (ref["kept"], ref["extra"])
+        sp = np.flatnonzero(~ref["dense"])
+        dn = np.flatnonzero(ref["dense"])
+        for pick, bucket, n in ((sp, t_sparse, n_sparse), (dn, t_dense, n_dense)):
+            if pick.size == 0:
+                continue
+            for i in rng.choice(pick, size=min(n, pick.size), replace=False):
+                t0 = time.perf_counter()
+                solattn.head_forward(w.mode, *xin, **p, selection=sel, qblocks=[int(i)])
+                bucket.append(time.perf_counter() - t0 - 0.0)
+    Mq = w.N // w.block_q
+    nd = (w.dense_rows[1] - w.dense_rows[0]) // w.block_q
+    BH = w.B * w.H
+    # the per-qblock timings above include pooling and scoring of the head once per call;
+    # subtract that fixed part by timing a run with no query blocks
+    xin = [a[0, heads[0]].astype(np.float64) for a in (x.q, x.k, x.v)]
+    t0 = time.perf_counter()
+    solattn.head_forward(w.mode, *xin, **p, selection=sel, qblocks=[])
+    fixed = time.perf_counter() - t0
+    per_sparse = max(0.0, float(np.mean(t_sparse)) - fixed) if t_sparse else 0.0
+    per_dense = max(0.0, float(np.mean(t_dense)) - fixed) if t_dense else 0.0
+    total = BH * (float(np.mean(t_sel)) + (Mq - nd) * per_sparse + nd * per_dense)
+    sample = (f"{len(heads)} head(s) full selection ({np.mean(t_sel):.2f} s/head), "
+              f"{len(t_sparse)} sparse + {len(t_dense)} dense query blocks attended "
+              f"({per_sparse * 1e3:.1f} / {per_dense * 1e3:.1f} ms each); extrapolated to "
+              f"{BH} heads x {Mq} query blocks")
+    return dict(value=total * 1e3, unit="ms", cores=int(cores), kind="oracle", sample=sample)
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this path shards by (batch, head) with no exchange; "
+              "multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_scores_amd as sa
+    from gen import make_inputs, workload
+
+    w = workload(a.config)
+    if a.tau is not None:
+        w = workload(a.config, tau=a.tau)
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}")
+    t0 = time.perf_counter()
+    x = make_inputs(w)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+    if w.dtype == "bf16":
+        to = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k, v = to(x.q_bits), to(x.k_bits), to(x.v_bits)
+    else:
+        q, k, v = (torch.from_numpy(t).to(dev) for t in (x.q, x.k, x.v))
+    mode = sa.MODE_SOL if w.mode == "sol" else sa.MODE_SLA
+    out = torch.empty_like(q)
+    ws = sa.alloc_workspace(mode, q, w.block_q, w.block_k)
+
+    def step():
+        if w.mode == "sol":
+            sa.sol_attn(q, k, v, tau=w.tau, block_q=w.block_q, block_k=w.block_k,
+                        sink_range=w.sink_range, extra_tokens=w.extra_tokens,
+                        dense_rows=w.dense_rows, out=out, workspace=ws)
+        else:
+            sa.sla_attn(q, k, v, keep_percent=w.keep_percent, block_q=w.block_q,
+                        block_k=w.block_k, sink_range=w.sink_range,
+                        extra_tokens=w.extra_tokens, dense_rows=w.dense_rows, out=out,
+                        workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({a.warmup} calls)")
+
+    sa.timing_read()                 # drop anything recorded before
+    sa.timing_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(a.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    sa.timing_enable(False)
+    per_kernel = sa.timing_read()
+    ms_per_call = start.elapsed_time(end) / a.steps
+    log(f"[bench] {a.steps} calls: {ms_per_call:.3f} ms/call (wall {t_wall / a.steps * 1e3:.3f})")
+
+    if a.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 1 GiB device copies")
+
+    views = sa.selection_views(ws, mode, sa.BF16 if w.dtype == "bf16" else sa.FP32, w.B, w.H, w.N,
+                               w.d, w.block_q, w.block_k)
+    sel = {k_: v_.cpu().numpy() for k_, v_ in views.items()}
+    exact_pairs, cent_terms, kept_frac = selection_stats(sel, w, w.B, w.H)
+    f_exact = 4.0 * w.d * exact_pairs
+    f_cent = 4.0 * w.d * cent_terms
+    BH, Mq, M = w.B * w.H, w.N // w.block_q, w.N // w.block_k
+    es = 2 if w.dtype == "bf16" else 4
+
+    kern = {}
+    for name, (ms, n) in per_kernel.items():
+        if n:
+            kern[name] = dict(avg_ms=ms / n, launches=n)
+    t_flash = kern["sparse_flash_fwd"]["avg_ms"] * 1e-3
+    ach = f_exact / t_flash / 1e12
+    roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None,
+                kernel="sparse_flash_fwd", algorithmic_flop=f_exact)
+    # the other kernels against their own rooflines
+    pool_bytes = BH * (3 * w.N * w.d * es + (Mq + 2 * M) * w.d * 4)
+    if "block_pool" in kern:
+        t = kern["block_pool"]["avg_ms"] * 1e-3
+        kern["block_pool"].update(bound="hbm", achieved_GBs=round(pool_bytes / t / 1e9, 1),
+                                  frac=round(pool_bytes / t / 1e9 / PEAK_HBM_GBS, 4))
+    if "block_score" in kern:
+        t = kern["block_score"]["avg_ms"] * 1e-3
+        fl = 2.0 * BH * Mq * M * w.d
+        kern["block_score"].update(bound="fp32", achieved_TFLOPs=round(fl / t / 1e12, 2),
+                                   frac=round(fl / t / 1e12 / PEAK_FP32_TFLOPS, 4))
+    if "block_select" in kern:
+        t = kern["block_select"]["avg_ms"] * 1e-3
+        by = BH * Mq * (M * 4 + 8 + (M + 63) // 64 * 64) + 4 * int(sel["kept_cnt"].sum())
+        kern["block_select"].update(bound="hbm", achieved_GBs=round(by / t / 1e9, 1),
+                                    frac=round(by / t / 1e9 / PEAK_HBM_GBS, 4))
+    if "extra_select" in kern:
+        t = kern["extra_select"]["avg_ms"] * 1e-3
+        fl = 2.0 * 2.0 * BH * Mq * w.N * w.d        # two bf16 passes (hi/lo split of q̄)
+        kern["extra_select"].update(bound="mfma", achieved_TFLOPs=round(fl / t / 1e12, 2),
+                                    frac=round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4))
+    kern["sparse_flash_fwd"].update(bound="mfma", achieved_TFLOPs=round(ach, 2),
+                                    frac=round(ach / PEAK_BF16_TFLOPS, 4))
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        t0 = time.perf_counter()
+        cpu = cpu_baseline(w, x)
+        log(f"[bench] oracle sample took {time.perf_counter() - t0:.1f} s")
+
+    res = {
+        "metric": "sol-attn fwd ms/call + MFMA util, N=65536 H=24 d=128 bf16 tau=1.3",
+        "value": round(ms_per_call, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_call, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": w.mode, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "block_q": w.block_q, "block_k": w.block_k, "tau": w.tau,
+                   "keep_percent": w.keep_percent if w.mode == "sla" else None,
+                   "extra_tokens": w.extra_tokens, "sink_range": w.sink_range,
+                   "dense_rows": list(w.dense_rows)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "effective_tflops": round(f_exact / (ms_per_call * 1e-3) / 1e12, 2),
+        "mfma_util": round(f_exact / (ms_per_call * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kept_fraction": round(kept_frac, 4),
+        "exact_tflop": round(f_exact / 1e12, 4),
+        "centroid_tflop": round(f_cent / 1e12, 4),
+        "kernels": kern,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -98,6 +98,8 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   if (N % block_q || N % block_k) return fail(SOLATTN_ENOTSUP, "N=%d not a multiple of the block sizes", N);
   if (d0 % block_q || d1 % block_q) return fail(SOLATTN_ENOTSUP, "dense rows not block_q aligned");
   if ((int64_t)B * H > 65535) return fail(SOLATTN_ENOTSUP, "B*H=%lld too large", (long long)B * H);
+  for (int t = 0; t < 4; ++t)   // the kernels address up to 64 rows with 32-bit byte offsets
+    if (st[t].sn >= (int64_t(1) << 24)) return fail(SOLATTN_ENOTSUP, "row stride of %c too large", "qkvo"[t]);
   for (int t = 0; t < 4; ++t) {
     const void* p = t < 3 ? ins[t] : out;
     if ((reinterpret_cast<uintptr_t>(p) % 16) || ((st[t].sb * es) % 16) || ((st[t].sh * es) % 16) ||

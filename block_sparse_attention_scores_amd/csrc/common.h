@@ -44,8 +44,10 @@ struct Problem {
 };
 
 constexpr int MAX_EXTRA = 256;
-constexpr int EXTRA_SLACK = 128;                 // candidates one token chunk can add per row
-constexpr int EXTRA_CAP = MAX_EXTRA + EXTRA_SLACK;
+// Candidate buffer per query block of the extra-token selection.  It is cut back to the best
+// extra_tokens entries only when one more 128-token step could overflow it, which keeps the
+// number of selections per row to a handful.
+constexpr int EXTRA_CAP = 768;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

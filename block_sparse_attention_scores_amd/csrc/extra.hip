@@ -67,7 +67,9 @@ __device__ int wave_pick_digit(const int* h, int need, int* above, int* at, int*
   return dg;
 }
 
-// Radix selection over 32-bit keys held 6 per lane (valid[] marks live entries).  Finds the
+constexpr int XPL = EXTRA_CAP / 64;   // buffer entries per lane during a selection
+
+// Radix selection over 32-bit keys held XPL per lane (valid[] marks live entries).  Finds the
 // `need`-th largest key K*, returns it; *need_eq = how many entries equal to K* are taken and
 // *cnt_eq = how many entries equal K*.
 __device__ uint32_t wave_radix_select(const uint32_t* key, const bool* valid, int need, int* hist,
@@ -81,7 +83,7 @@ __device__ uint32_t wave_radix_select(const uint32_t* key, const bool* valid, in
     for (int q = 0; q < 4; ++q) hist[4 * l + q] = 0;
     wave_sync();
 #pragma unroll
-    for (int u = 0; u < 6; ++u)
+    for (int u = 0; u < XPL; ++u)
       if (valid[u] && (key[u] & pmask) == prefix) atomicAdd(&hist[(key[u] >> shift) & 255u], 1);
     wave_sync();
     int above;
@@ -98,10 +100,10 @@ __device__ uint32_t wave_radix_select(const uint32_t* key, const bool* valid, in
 // Reduce one row's buffer (cnt > E entries) to its E best entries under (score desc, token asc).
 __device__ float wave_compact_row(uint2* buf, int cnt, int E, int* hist, int* scratch) {
   const int l = threadIdx.x & 63;
-  uint32_t key[6], tok[6];
-  bool valid[6];
+  uint32_t key[XPL], tok[XPL];
+  bool valid[XPL];
 #pragma unroll
-  for (int u = 0; u < 6; ++u) {
+  for (int u = 0; u < XPL; ++u) {
     const int p = l + 64 * u;
     valid[u] = p < cnt;
     uint2 e = valid[u] ? buf[p] : make_uint2(0u, 0u);
@@ -112,10 +114,10 @@ __device__ float wave_compact_row(uint2* buf, int cnt, int E, int* hist, int* sc
   const uint32_t kstar = wave_radix_select(key, valid, E, hist, scratch, &need_eq, &cnt_eq);
   uint32_t tmax = 0xFFFFFFFFu;   // largest token taken among those tying K*
   if (need_eq < cnt_eq) {
-    uint32_t k2[6];
-    bool v2[6];
+    uint32_t k2[XPL];
+    bool v2[XPL];
 #pragma unroll
-    for (int u = 0; u < 6; ++u) {
+    for (int u = 0; u < XPL; ++u) {
       v2[u] = valid[u] && key[u] == kstar;
       k2[u] = ~tok[u];            // larger k2 = smaller token
     }
@@ -123,14 +125,14 @@ __device__ float wave_compact_row(uint2* buf, int cnt, int E, int* hist, int* sc
     const uint32_t t2 = wave_radix_select(k2, v2, need_eq, hist, scratch, &ne2, &ce2);
     tmax = ~t2;
   }
-  bool keep[6];
+  bool keep[XPL];
 #pragma unroll
-  for (int u = 0; u < 6; ++u)
+  for (int u = 0; u < XPL; ++u)
     keep[u] = valid[u] && (key[u] > kstar || (key[u] == kstar && tok[u] <= tmax));
   // every lane holds its entries in registers now; write the survivors to the front
   int base = 0;
 #pragma unroll
-  for (int u = 0; u < 6; ++u) {
+  for (int u = 0; u < XPL; ++u) {
     const uint64_t m = __ballot(keep[u]);
     const int pos = base + __popcll(m & ((1ull << l) - 1ull));
     if (keep[u]) buf[pos] = make_uint2(__float_as_uint(key_float(key[u])), tok[u]);
@@ -226,9 +228,12 @@ __global__ __launch_bounds__(256) void extra_select_kernel(Problem P) {
       }
     }
     __syncthreads();
+    // cut a buffer back to its E best entries when the next step could overflow it, and
+    // after the last step
+    const bool last = t0 + XCHUNK >= N;
     for (int rr = w; rr < XR; rr += 4) {
       const int c = cnt[rr];
-      if (c > E) {
+      if (c > EXTRA_CAP - XCHUNK || (last && c > E)) {
         uint2* rb = P.extra_buf + ((size_t)bh * P.Mq + i0 + rr) * EXTRA_CAP;
         const float th = wave_compact_row(rb, c, E, whist[w], wscr[w]);
         if (l == 0) {

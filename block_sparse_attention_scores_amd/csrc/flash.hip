@@ -27,15 +27,336 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float LOG2E = 1.4426950408889634f;
 
+// ------------------------------------------------------------------ bf16 path
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Asynchronous 16-byte global -> LDS copy: lane l's 16 bytes land at `wave_dst` + 16*l, where
+// `wave_dst` is the same for the whole wave.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* wave_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(wave_dst), 16, 0, 0);
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Double-buffered LDS tiles.  K: 64 keys x D, 16-byte chunks of each row XOR-swizzled by the row
+// index.  V: either the transposed tile (D rows of 64 keys, chunks swizzled by row) or, for
+// gathered extra tokens, plain row-major 64 x D.  Bias: per query block of the pair, per key.
 template <int D>
 struct FlashSmem {
-  uint16_t k[64][D + 8];      // K tile, key-major, padded rows
-  uint16_t vt[D][64 + 8];     // V tile transposed (d-major), keys permuted by vt_pos
-  float bias[64];             // additive base-2 logit bias per key of the tile
+  uint16_t k[2][64 * D];
+  uint16_t v[2][64 * D];
+  float bias[2][2][64];
 };
 
-// Map the flat workgroup index to (head, query block): dense query blocks (the heaviest work)
-// first, and consecutive workgroups on the same head.
+struct TileDesc {
+  int kind;   // 0 kept key block, 1 extra tokens of one query block, 2 centroids, 3 end
+  int idx;    // key block j | first extra position | first centroid index
+  int sel;    // bit g: query block g of the pair attends this tile
+};
+
+// Walks the pipelined work of a pair of query blocks: the union of their kept-block lists
+// (merged in ascending order), then the centroid tiles.  Every thread holds identical state, so
+// all decisions are uniform.  (Extra tokens are gathered in a separate pass afterwards.)
+struct TileIter {
+  const int* list0;
+  const int* list1;
+  int n0, n1, p0, p1;
+  int pos, ncent, cent_sel;
+  __device__ TileDesc next() {
+    const int a = p0 < n0 ? uniform(list0[p0]) : 0x7fffffff;
+    const int b = p1 < n1 ? uniform(list1[p1]) : 0x7fffffff;
+    if (a != 0x7fffffff || b != 0x7fffffff) {
+      const int j = a < b ? a : b;
+      const int sel = (a == j ? 1 : 0) | (b == j ? 2 : 0);
+      p0 += a == j;
+      p1 += b == j;
+      return TileDesc{0, j, sel};
+    }
+    if (pos < ncent) {
+      const int c = pos;
+      pos += 64;
+      return TileDesc{2, c, cent_sel};
+    }
+    return TileDesc{3, 0, 0};
+  }
+};
+
+// Workgroup -> (head, pair of query blocks).  Pairs overlapping the dense row range (the
+// heaviest) come first, then the rest head-major.  Consecutive units go to the same XCD in runs
+// of XCD_RUN (workgroups are dealt to the 8 XCDs round-robin), so one XCD works on neighbouring
+// query blocks of one head and shares their key tiles in its L2.
+constexpr int XCD_RUN = 16;
+
+__device__ __forceinline__ bool flash_unit(const Problem& P, int G, int gid, int* bh, int* pair) {
+  const int x = gid % 8, k = gid / 8;
+  const int u = (k / XCD_RUN) * 8 * XCD_RUN + x * XCD_RUN + (k % XCD_RUN);
+  const int Mp = (P.Mq + G - 1) / G;
+  const int BH = P.B * P.H;
+  int h0 = 0, h1 = 0;
+  if (P.dense_q1 > P.dense_q0) {
+    h0 = P.dense_q0 / G;
+    h1 = (P.dense_q1 + G - 1) / G;
+  }
+  const int nh = h1 - h0;
+  if (u >= BH * Mp) return false;
+  if (u < BH * nh) {
+    *bh = u / nh;
+    *pair = h0 + u % nh;
+    return true;
+  }
+  const int v = u - BH * nh;
+  const int ns = Mp - nh;
+  *bh = v / ns;
+  const int r = v % ns;
+  *pair = r < h0 ? r : r + nh;
+  return true;
+}
+
+// WPQ waves per query block (block_q / 32), G query blocks per workgroup; WPQ * G = 4.
+template <int D, int WPQ, int G>
+__global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
+  __shared__ FlashSmem<D> sm;
+  constexpr int KCH = D / 8;                 // 16-byte chunks per K row
+  constexpr int SLOTS = 64 * D / 8;          // 16-byte slots per tile matrix
+  constexpr int PER_THREAD = SLOTS / 256;
+  int bh, pair;
+  if (!flash_unit(P, G, blockIdx.x, &bh, &pair)) return;
+  const int tid = threadIdx.x, w = tid / 64, l = tid % 64, h32 = l / 32, c32 = l % 32;
+  const int g = w / WPQ;                     // this wave's query block within the pair
+  const int b = bh / P.H, hh = bh % P.H;
+  const uint16_t* Kb = static_cast<const uint16_t*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)hh * P.k.sh;
+  const uint16_t* Vb = static_cast<const uint16_t*>(P.v.p) + (int64_t)b * P.v.sb + (int64_t)hh * P.v.sh;
+  const uint16_t* Qb = static_cast<const uint16_t*>(P.q.p) + (int64_t)b * P.q.sb + (int64_t)hh * P.q.sh;
+
+  // per query block of the pair
+  int qb[2], nk[2], ne[2];
+  bool dense[2], valid[2];
+  const int* klist[2];
+  const int* elist[2];
+  const uint8_t* mrow[2];
+#pragma unroll
+  for (int gg = 0; gg < 2; ++gg) {
+    qb[gg] = pair * G + gg;
+    valid[gg] = gg < G && qb[gg] < P.Mq;
+    const int qq = valid[gg] ? qb[gg] : pair * G;
+    const size_t row = (size_t)bh * P.Mq + qq;
+    dense[gg] = qq >= P.dense_q0 && qq < P.dense_q1;
+    nk[gg] = valid[gg] ? uniform(P.kept_cnt[row]) : 0;
+    ne[gg] = (valid[gg] && !dense[gg]) ? uniform(P.extra_cnt[row]) : 0;
+    klist[gg] = P.kept_idx + row * P.M;
+    elist[gg] = P.extra_idx + row * MAX_EXTRA;
+    mrow[gg] = P.mult + row * P.Mpad;
+  }
+  int cent_sel = 0;
+  if (P.mode == 0) {
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+      if (valid[gg] && !dense[gg] && nk[gg] < P.M) cent_sel |= 1 << gg;
+  }
+  TileIter it{klist[0], klist[1], nk[0], nk[1], 0, 0, 0, cent_sel ? P.Mpad : 0, cent_sel};
+
+  // this wave's 32 query rows: Q^T operand fragments
+  const bool wave_on = valid[g];
+  const int q0 = (valid[g] ? qb[g] : qb[0]) * P.bq + 32 * (w % WPQ);
+  bf16x8_t qf[D / 16];
+  {
+    const uint16_t* qr = Qb + (int64_t)(q0 + c32) * P.q.sn + 8 * h32;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * ks);
+  }
+
+  // ---- issue the asynchronous loads of one tile into buffer bf.  Sources are a uniform base
+  // pointer plus a 32-bit per-lane byte offset (row strides are bounded on the host).
+  const uint32_t ksn_b = static_cast<uint32_t>(P.k.sn) * 2u;
+  const uint32_t vsn_b = static_cast<uint32_t>(P.v.sn) * 2u;
+  auto issue = [&](const TileDesc& t, int bf) {
+    uint16_t* kd = sm.k[bf];
+    uint16_t* vd = sm.v[bf];
+    const char* kbase;
+    uint32_t krow_b;
+    const char* vbase;
+    if (t.kind == 0) {
+      kbase = reinterpret_cast<const char*>(Kb + (int64_t)t.idx * 64 * P.k.sn);
+      krow_b = ksn_b;
+      vbase = reinterpret_cast<const char*>(P.v_t + ((size_t)bh * P.M + t.idx) * D * 64);
+    } else {
+      kbase = reinterpret_cast<const char*>(P.kbar_bf + ((size_t)bh * P.Mpad + t.idx) * D);
+      krow_b = D * 2;
+      vbase = reinterpret_cast<const char*>(P.vbar_t + ((size_t)bh * (P.Mpad / 64) + t.idx / 64) * D * 64);
+    }
+#pragma unroll
+    for (int u = 0; u < PER_THREAD; ++u) {
+      const int s = (u * 4 + w) * 64 + l;
+      const int r = s / KCH, c = s % KCH;
+      copy16_to_lds(kbase + (uint32_t)r * krow_b + (uint32_t)((c ^ (r & (KCH - 1))) * 16),
+                    kd + (u * 4 + w) * 64 * 8);
+      const int vr = s / 8, vc = s % 8;
+      copy16_to_lds(vbase + (uint32_t)(vr * 128 + (vc ^ (vr & 7)) * 16), vd + (u * 4 + w) * 64 * 8);
+    }
+    if (t.kind == 2 && tid < 128) {
+      const int gg = tid / 64, key = tid % 64;
+      float bv = -__builtin_inff();
+      if ((t.sel >> gg) & 1) {
+        const int m = mrow[gg][t.idx + key];   // 0: kept block or padding beyond M
+        bv = m > 0 ? __log2f(static_cast<float>(m)) : -__builtin_inff();
+      }
+      sm.bias[bf][gg][key] = bv;
+    }
+  };
+
+  f32x16_t o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+  const float sl2 = P.scale * LOG2E;
+
+  // ---- one tile for this wave's 32 query rows
+  auto compute = [&](const TileDesc& t, int bf) {
+    const uint16_t* kt_ = sm.k[bf];
+    const uint16_t* vt_ = sm.v[bf];
+    f32x16_t s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      s[kt] = f32x16_t{};
+      const int r = 32 * kt + c32;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int c = (2 * ks + h32) ^ (r & (KCH - 1));
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt_ + r * D + c * 8);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
+      }
+    }
+    // register r of half kt holds key 32kt + (r/4)*8 + 4*h32 + r%4
+    float mx = -__builtin_inff();
+    if (t.kind == 0) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[kt][r] *= sl2;
+          mx = fmaxf(mx, s[kt][r]);
+        }
+    } else {   // centroid and extra-token tiles carry a per-key bias
+      const float* bias = sm.bias[bf][g];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kt + (r / 4) * 8 + 4 * h32 + (r % 4);
+          s[kt][r] = fmaf(s[kt][r], sl2, bias[key]);
+          mx = fmaxf(mx, s[kt][r]);
+        }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(s[kt][r] - m_use);
+        psum += p;
+        s[kt][r] = p;
+      }
+    l_run = fmaf(l_run, alpha, psum);
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    // O^T += V^T P^T, one 16-key step at a time: P^T for keys 16ks.. is registers
+    // 8(ks%2)..+8 of score half ks/2
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = static_cast<__bf16>(s[ks / 2][8 * (ks % 2) + e]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int r = 32 * dt + c32;
+        const int c = (2 * ks + h32) ^ (r & 7);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vt_ + r * 64 + c * 8);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, o[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  TileDesc cur = it.next();
+  int bf = 0;
+  issue(cur, 0);
+  for (;;) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const TileDesc nxt = it.next();
+    if (nxt.kind != 3) issue(nxt, bf ^ 1);
+    if (wave_on && ((cur.sel >> g) & 1)) compute(cur, bf);
+    if (nxt.kind == 3) break;
+    cur = nxt;
+    bf ^= 1;
+  }
+
+  // ---- extra tokens: up to 4 gathered 64-token tiles per query block, loaded synchronously.
+  // K rows go straight to LDS; V rows pass through registers and are stored transposed (with
+  // the same key permutation and swizzle as the pre-transposed tiles).
+#pragma unroll 1
+  for (int gg = 0; gg < G; ++gg) {
+    const int cnt = ne[gg];
+    const int* el = elist[gg];
+#pragma unroll 1
+    for (int e0 = 0; e0 < cnt; e0 += 64) {
+      __syncthreads();
+      uint16_t* kd = sm.k[0];
+      uint16_t* vd = sm.v[0];
+#pragma unroll
+      for (int u = 0; u < PER_THREAD; ++u) {
+        const int sl = (u * 4 + w) * 64 + l;
+        const int r = sl / KCH, c = sl % KCH;
+        const int e = e0 + r < cnt ? e0 + r : e0;               // padding rows reuse a real token
+        const uint32_t tok = static_cast<uint32_t>(el[e]);
+        copy16_to_lds(reinterpret_cast<const char*>(Kb) + (size_t)tok * ksn_b + ((c ^ (r & (KCH - 1))) * 16),
+                      kd + (u * 4 + w) * 64 * 8);
+        const uint4 vv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Vb) +
+                                                         (size_t)tok * vsn_b + c * 16);
+        const uint16_t* vx = reinterpret_cast<const uint16_t*>(&vv);
+        const int pos = vt_pos(r);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int dr = c * 8 + x;                           // d row of the transposed tile
+          vd[dr * 64 + (((pos >> 3) ^ (dr & 7)) << 3) + (pos & 7)] = vx[x];
+        }
+      }
+      if (tid < 64) sm.bias[0][gg][tid] = e0 + tid < cnt ? 0.f : -__builtin_inff();
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (wave_on && g == gg) compute(TileDesc{1, e0, 1 << gg}, 0);
+    }
+  }
+
+  if (!wave_on) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.f / l_tot;
+  uint16_t* Ob = static_cast<uint16_t*>(const_cast<void*>(P.o.p)) + (int64_t)b * P.o.sb +
+                 (int64_t)hh * P.o.sh + (int64_t)(q0 + c32) * P.o.sn;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d0 = 32 * dt + 8 * gq + 4 * h32;
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      bf16x4_t pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = static_cast<__bf16>(o[dt][4 * gq + e] * inv);
+      *reinterpret_cast<bf16x4_t*>(Ob + d0) = pk;
+    }
+}
+
+// ------------------------------------------------------------------ fp32 path
+
+// fp32 path: workgroup -> (head, query block), dense query blocks (the heaviest) first.
 __device__ __forceinline__ void flash_work(const Problem& P, int g, int* bh, int* qi) {
   const int nd = P.dense_q1 - P.dense_q0;
   const int BH = P.B * P.H;
@@ -47,172 +368,9 @@ __device__ __forceinline__ void flash_work(const Problem& P, int g, int* bh, int
   g -= BH * nd;
   const int ns = P.Mq - nd;
   *bh = g / ns;
-  int r = g % ns;
+  const int r = g % ns;
   *qi = r < P.dense_q0 ? r : r + nd;
 }
-
-template <int D, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void sparse_flash_bf16_kernel(Problem P) {
-  __shared__ FlashSmem<D> sm;
-  constexpr int NT = 64 * WAVES;
-  int bh, qi;
-  flash_work(P, blockIdx.x, &bh, &qi);
-  const int tid = threadIdx.x, w = tid / 64, l = tid % 64, h32 = l / 32, c32 = l % 32;
-  const int b = bh / P.H, hh = bh % P.H;
-  const size_t row = (size_t)bh * P.Mq + qi;
-  const uint16_t* Kb = static_cast<const uint16_t*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)hh * P.k.sh;
-  const uint16_t* Vb = static_cast<const uint16_t*>(P.v.p) + (int64_t)b * P.v.sb + (int64_t)hh * P.v.sh;
-  const uint16_t* Qb = static_cast<const uint16_t*>(P.q.p) + (int64_t)b * P.q.sb + (int64_t)hh * P.q.sh;
-
-  // this wave's 32 query rows: Q^T operand fragments
-  const int q0 = qi * P.bq + 32 * w;
-  bf16x8_t qf[D / 16];
-  {
-    const uint16_t* qr = Qb + (int64_t)(q0 + c32) * P.q.sn + 8 * h32;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * ks);
-  }
-
-  const bool dense = qi >= P.dense_q0 && qi < P.dense_q1;
-  const int nk = P.kept_cnt[row];
-  const int ne = dense ? 0 : P.extra_cnt[row];
-  const int nx = (ne + 63) / 64;
-  const int nc = (P.mode == 0 && !dense && nk < P.M) ? P.Mpad / 64 : 0;
-  const int ntiles = nk + nx + nc;
-  const int* klist = P.kept_idx + row * P.M;
-  const int* elist = P.extra_idx + row * MAX_EXTRA;
-  const uint8_t* mrow = P.mult + row * P.Mpad;
-  const float sl2 = P.scale * LOG2E;
-
-  f32x16_t o[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
-
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    // ---- stage the tile in LDS
-    if (t < nk) {
-      const int j = klist[t];
-      const uint16_t* ks = Kb + (int64_t)j * 64 * P.k.sn;
-      for (int u = tid; u < 64 * (D / 8); u += NT) {
-        const int r = u / (D / 8), c = (u % (D / 8)) * 8;
-        *reinterpret_cast<uint4*>(&sm.k[r][c]) = *reinterpret_cast<const uint4*>(ks + (int64_t)r * P.k.sn + c);
-      }
-      const uint16_t* vs = P.v_t + ((size_t)bh * P.M + j) * D * 64;
-      for (int u = tid; u < D * 8; u += NT) {
-        const int r = u / 8, c = (u % 8) * 8;
-        *reinterpret_cast<uint4*>(&sm.vt[r][c]) = *reinterpret_cast<const uint4*>(vs + r * 64 + c);
-      }
-      if (tid < 64) sm.bias[tid] = 0.f;
-    } else if (t < nk + nx) {
-      const int e0 = (t - nk) * 64;
-      for (int u = tid; u < 64 * (D / 8); u += NT) {
-        const int r = u / (D / 8), c = (u % (D / 8)) * 8;
-        uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
-        if (e0 + r < ne) {
-          const int tok = elist[e0 + r];
-          kv = *reinterpret_cast<const uint4*>(Kb + (int64_t)tok * P.k.sn + c);
-          vv = *reinterpret_cast<const uint4*>(Vb + (int64_t)tok * P.v.sn + c);
-        }
-        *reinterpret_cast<uint4*>(&sm.k[r][c]) = kv;
-        const uint16_t* vx = reinterpret_cast<const uint16_t*>(&vv);
-        const int pr = vt_pos(r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm.vt[c + e][pr] = vx[e];
-      }
-      if (tid < 64) sm.bias[tid] = (e0 + tid < ne) ? 0.f : -__builtin_inff();
-    } else {
-      const int c0 = (t - nk - nx) * 64;
-      const uint16_t* ks = P.kbar_bf + ((size_t)bh * P.Mpad + c0) * D;
-      for (int u = tid; u < 64 * (D / 8); u += NT) {
-        const int r = u / (D / 8), c = (u % (D / 8)) * 8;
-        *reinterpret_cast<uint4*>(&sm.k[r][c]) = *reinterpret_cast<const uint4*>(ks + (size_t)r * D + c);
-      }
-      const uint16_t* vs = P.vbar_t + ((size_t)bh * (P.Mpad / 64) + c0 / 64) * D * 64;
-      for (int u = tid; u < D * 8; u += NT) {
-        const int r = u / 8, c = (u % 8) * 8;
-        *reinterpret_cast<uint4*>(&sm.vt[r][c]) = *reinterpret_cast<const uint4*>(vs + r * 64 + c);
-      }
-      if (tid < 64) {
-        const int m = mrow[c0 + tid];    // 0 for kept blocks and for padding beyond M
-        sm.bias[tid] = m > 0 ? __log2f(static_cast<float>(m)) : -__builtin_inff();
-      }
-    }
-    __syncthreads();
-
-    // ---- S^T = K Q^T for the 64 keys (two 32-key halves)
-    f32x16_t s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sm.k[32 * kt + c32][16 * ks + 8 * h32]);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
-      }
-    }
-    // ---- online softmax (base 2); register r of half kt holds key 32kt + (r/4)*8 + 4*h32 + r%4
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + (r / 4) * 8 + 4 * h32 + (r % 4);
-        const float x = s[kt][r] * sl2 + sm.bias[key];
-        s[kt][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float psum = 0.f;
-    bf16x8_t pf[4];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(s[kt][r] - m_use);
-        psum += p;
-        pf[2 * kt + r / 8][r % 8] = __builtin_bit_cast(__bf16, f32_to_bf16(p));
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sm.vt[32 * dt + c32][16 * ks + 8 * h32]);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[dt], 0, 0, 0);
-      }
-  }
-
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / l_tot;
-  uint16_t* Ob = static_cast<uint16_t*>(const_cast<void*>(P.o.p)) + (int64_t)b * P.o.sb +
-                 (int64_t)hh * P.o.sh + (int64_t)(q0 + c32) * P.o.sn;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = 32 * dt + 8 * g + 4 * h32;
-      uint2 pk;
-      pk.x = static_cast<uint32_t>(f32_to_bf16(o[dt][4 * g + 0] * inv)) |
-             (static_cast<uint32_t>(f32_to_bf16(o[dt][4 * g + 1] * inv)) << 16);
-      pk.y = static_cast<uint32_t>(f32_to_bf16(o[dt][4 * g + 2] * inv)) |
-             (static_cast<uint32_t>(f32_to_bf16(o[dt][4 * g + 3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(Ob + d0) = pk;
-    }
-}
-
-// ------------------------------------------------------------------ fp32 path
 
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ) void sparse_flash_f32_kernel(Problem P) {
@@ -320,16 +478,21 @@ __global__ __launch_bounds__(BQ) void sparse_flash_f32_kernel(Problem P) {
 }
 
 hipError_t launch_sparse_flash(const Problem& P, hipStream_t stream) {
-  dim3 grid(P.B * P.H * P.Mq);
   if (P.dtype == 0) {
+    const int G = P.bq == 64 ? 2 : 1;
+    const int Mp = (P.Mq + G - 1) / G;
+    const int units = P.B * P.H * Mp;
+    const int per_round = 8 * XCD_RUN;
+    dim3 grid((units + per_round - 1) / per_round * per_round);
     if (P.bq == 64) {
-      if (P.d == 128) hipLaunchKernelGGL((sparse_flash_bf16_kernel<128, 2>), grid, dim3(128), 0, stream, P);
-      else hipLaunchKernelGGL((sparse_flash_bf16_kernel<64, 2>), grid, dim3(128), 0, stream, P);
+      if (P.d == 128) hipLaunchKernelGGL((sparse_flash_bf16_kernel<128, 2, 2>), grid, dim3(256), 0, stream, P);
+      else hipLaunchKernelGGL((sparse_flash_bf16_kernel<64, 2, 2>), grid, dim3(256), 0, stream, P);
     } else {
-      if (P.d == 128) hipLaunchKernelGGL((sparse_flash_bf16_kernel<128, 4>), grid, dim3(256), 0, stream, P);
-      else hipLaunchKernelGGL((sparse_flash_bf16_kernel<64, 4>), grid, dim3(256), 0, stream, P);
+      if (P.d == 128) hipLaunchKernelGGL((sparse_flash_bf16_kernel<128, 4, 1>), grid, dim3(256), 0, stream, P);
+      else hipLaunchKernelGGL((sparse_flash_bf16_kernel<64, 4, 1>), grid, dim3(256), 0, stream, P);
     }
   } else {
+    dim3 grid(P.B * P.H * P.Mq);
     if (P.bq == 64) {
       if (P.d == 128) hipLaunchKernelGGL((sparse_flash_f32_kernel<128, 64>), grid, dim3(64), 0, stream, P);
       else hipLaunchKernelGGL((sparse_flash_f32_kernel<64, 64>), grid, dim3(64), 0, stream, P);

@@ -26,6 +26,7 @@ Every (batch, head) has its own counter-free numpy PCG64 stream seeded by
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field, replace
 
 import numpy as np
@@ -131,8 +132,10 @@ def latent_field(w: Workload, b: int = 0) -> np.ndarray:
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 to the nearest bfloat16 (ties to even); returns the uint16 bit patterns."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
     return r.astype(np.uint16)
 
 
@@ -168,8 +171,14 @@ class Inputs:
     v_bits: np.ndarray | None = None
 
 
-def make_inputs(w: Workload | int, heads=None) -> Inputs:
-    """Draw Q, K, V for workload ``w`` (all heads, or the listed subset)."""
+def make_inputs(w: Workload | int, heads=None, threads: int | None = None) -> Inputs:
+    """Draw Q, K, V for workload ``w`` (all heads, or the listed subset).
+
+    Heads are drawn in parallel threads; each has its own random stream, so the result does
+    not depend on the thread count.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
     if isinstance(w, int):
         w = WORKLOADS[w]
     heads = tuple(range(w.H)) if heads is None else tuple(heads)
@@ -177,9 +186,12 @@ def make_inputs(w: Workload | int, heads=None) -> Inputs:
     bf = w.dtype == "bf16"
     out = {n: np.empty(shape, np.float32) for n in "qkv"}
     bits = {n: np.empty(shape, np.uint16) for n in "qkv"} if bf else None
+    nthr = threads or min(8, os.cpu_count() or 1)
     for b in range(w.B):
         z = latent_field(w, b)
-        for hi, h in enumerate(heads):
+
+        def one(item):
+            hi, h = item
             for name, x in zip("qkv", head_tensors(w, z, b, h)):
                 if bf:
                     bb = bf16_round(x)
@@ -187,6 +199,9 @@ def make_inputs(w: Workload | int, heads=None) -> Inputs:
                     out[name][b, hi] = bf16_to_f32(bb)
                 else:
                     out[name][b, hi] = x
+
+        with ThreadPoolExecutor(max_workers=nthr) as ex:
+            list(ex.map(one, enumerate(heads)))
     if bf:
         return Inputs(w, heads, out["q"], out["k"], out["v"], bits["q"], bits["k"], bits["v"])
     return Inputs(w, heads, out["q"], out["k"], out["v"])

@@ -126,7 +126,7 @@ int solattn_check_args(int mode, const void* q, const void* k, const void* v, vo
  *   mult      uint8 [B*H, Mq, Mpad] centroid multiplicity of each key block (0 = attended exactly)
  *   extra_cnt int32 [B*H, Mq]      number of extra tokens
  *   extra_idx int32 [B*H, Mq, 256] extra token indices, ascending, first extra_cnt valid
- *   extra_buf 8-byte entries [B*H, Mq, 384]: scratch of the extra-token selection
+ *   extra_buf 8-byte entries [B*H, Mq, 768]: scratch of the extra-token selection
  *   kbar_bf   bf16 [B*H, Mpad, d], vbar_t bf16 [B*H, Mpad/64, d, 64], v_t bf16
  *             [B*H, M, d, 64]: operand copies for the attention kernel (bf16 only)
  * Mq = N/block_q, M = N/block_k, Mpad = M rounded up to a multiple of 64.
