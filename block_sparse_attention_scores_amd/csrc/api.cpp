@@ -131,9 +131,12 @@ int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int blo
   L->kept_cnt = take(BH * Mq * 4);
   L->kept_idx = take(BH * Mq * M * 4);
   L->mult = take(BH * Mq * Mpad);
+  L->cbias = take(BH * Mq * Mpad * 4);
   L->extra_cnt = take(BH * Mq * 4);
   L->extra_idx = take(BH * Mq * SOLATTN_MAX_EXTRA * 4);
-  L->extra_buf = take(BH * Mq * solattn::EXTRA_CAP * 8);
+  const int S = solattn::extra_slice_count(B, H, Mq);
+  L->extra_buf = take(BH * Mq * S * 4 * solattn::EXTRA_CAP * 8);
+  L->extra_part = take(BH * Mq * S * 4 * 4);
   if (dtype == SOLATTN_BF16) {
     L->kbar_bf = take(BH * Mpad * d * 2);
     L->vbar_t = take(BH * Mpad * d * 2);
@@ -244,9 +247,12 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   P.kept_cnt = reinterpret_cast<int*>(ws + L.kept_cnt);
   P.kept_idx = reinterpret_cast<int*>(ws + L.kept_idx);
   P.mult = reinterpret_cast<uint8_t*>(ws + L.mult);
+  P.cbias = reinterpret_cast<float*>(ws + L.cbias);
   P.extra_cnt = reinterpret_cast<int*>(ws + L.extra_cnt);
   P.extra_idx = reinterpret_cast<int*>(ws + L.extra_idx);
   P.extra_buf = reinterpret_cast<uint2*>(ws + L.extra_buf);
+  P.extra_part = reinterpret_cast<int*>(ws + L.extra_part);
+  P.extra_slices = solattn::extra_slice_count(B, H, L.Mq);
   if (dtype == SOLATTN_BF16) {
     P.kbar_bf = reinterpret_cast<uint16_t*>(ws + L.kbar_bf);
     P.vbar_t = reinterpret_cast<uint16_t*>(ws + L.vbar_t);

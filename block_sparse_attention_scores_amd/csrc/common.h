@@ -35,19 +35,29 @@ struct Problem {
   int* kept_cnt;
   int* kept_idx;
   uint8_t* mult;
+  float* cbias;          // ln(centroid multiplicity) / scale (a raw-score offset), -inf where it is 0
   int* extra_cnt;
   int* extra_idx;
-  uint2* extra_buf;      // per query block: (score bits, token) candidate buffer, EXTRA_CAP entries
+  uint2* extra_buf;      // per query block, token slice and wave: (score bits, token) candidates
+  int* extra_part;       // per query block, token slice and wave: entries left after the final cut
+  int extra_slices;      // token slices of the extra-token selection
   uint16_t* kbar_bf;
   uint16_t* vbar_t;
   uint16_t* v_t;
 };
 
 constexpr int MAX_EXTRA = 256;
-// Candidate buffer per query block of the extra-token selection.  It is cut back to the best
-// extra_tokens entries only when one more 128-token step could overflow it, which keeps the
-// number of selections per row to a handful.
-constexpr int EXTRA_CAP = 768;
+// Candidate buffer per (query block, token slice, wave) of the extra-token selection.  It is cut
+// back to the best extra_tokens entries only when one more 32-token step could overflow it,
+// which for the workloads here almost never happens.
+constexpr int EXTRA_CAP = 1024;
+
+// Token slices of the extra-token selection: enough workgroups to fill the chip, at most 4.
+__host__ __device__ inline int extra_slice_count(int B, int H, int Mq) {
+  const long groups = (long)((Mq + 31) / 32) * B * H;
+  long s = (1536 + groups - 1) / groups;
+  return s < 1 ? 1 : (s > 4 ? 4 : (int)s);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -3,17 +3,22 @@
 // docs, common inputs table, extra_tokens row: extra high-score tokens each query block
 // attends beyond its selected blocks).
 //
-// A workgroup (4 waves) owns 32 query blocks of one head and streams the head's keys once,
-// 128 tokens per step (32 per wave).  Scores come from the 32x32x16 bf16 matrix instruction
-// with q̄ split into two bf16 parts (hi + lo), so each score is accurate to ~2^-17 relative,
-// i.e. fp32-like, while the keys are exact bf16.  Each lane owns one query block (column of
-// the 32x32 accumulator); a score above the row's running threshold is appended to the row's
-// candidate buffer in the workspace.  When a buffer holds more than E entries after a step,
-// one wave finds the E-th best entry by radix selection on (score, token) and compacts the
-// buffer to exactly E entries; that entry's score becomes the new threshold.  Keys stream in
-// increasing token order, so a later token that ties the threshold always loses the tie and a
-// strict comparison suffices.  At the end the E tokens are ranked ascending, written out, and
-// the centroid multiplicity of every block they came from drops by their count.
+// Pass 1 (extra_select_kernel).  A workgroup of 4 waves owns 32 query blocks of one head and one
+// slice of the token range; the waves take turns over 32-token steps.  Scores come from the
+// 32x32x16 bf16 matrix instruction with q̄ split into two bf16 parts (hi + lo), accurate to
+// ~2^-17 relative (fp32-like), while the keys are exact bf16.  Each lane owns one query block
+// (a column of the accumulator).  Every wave keeps its own candidate buffer per query block in
+// the workspace, so the streaming loop needs no barrier; the four waves share one running
+// threshold per query block in LDS (any wave's E-th best is a lower bound of the final E-th
+// best).  A score above the threshold is appended; when a buffer could overflow on the next
+// step, the wave finds its E-th best entry by radix selection on (score, token), cuts the
+// buffer to exactly E entries and raises the shared threshold.  Keys stream in increasing token
+// order within a wave, so a later token that ties the threshold loses the tie and a strict
+// comparison suffices.
+//
+// Pass 2 (extra_merge_kernel).  One wave per query block takes the best E of the partial lists
+// (one per wave and slice), ranks them by token, writes them out, and takes the chosen tokens
+// out of their blocks' centroid terms.
 #include "common.h"
 #include "launch.h"
 
@@ -23,14 +28,18 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int XR = 32;      // query blocks per workgroup
-constexpr int XCHUNK = 128; // tokens per step
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int XSTEP = 32;   // tokens per wave step
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   __builtin_amdgcn_wave_barrier();
 }
-
-__device__ __forceinline__ uint16_t bf16_bits(float f) { return f32_to_bf16(f); }
 
 // One radix digit step inside one wave: given the 256-bin histogram `h` (in LDS) of the
 // candidates still matching the prefix, find the digit holding the `need`-th largest.
@@ -67,11 +76,10 @@ __device__ int wave_pick_digit(const int* h, int need, int* above, int* at, int*
   return dg;
 }
 
-constexpr int XPL = EXTRA_CAP / 64;   // buffer entries per lane during a selection
-
-// Radix selection over 32-bit keys held XPL per lane (valid[] marks live entries).  Finds the
-// `need`-th largest key K*, returns it; *need_eq = how many entries equal to K* are taken and
+// Radix selection over 32-bit keys held NPL per lane (valid[] marks live entries).  Finds the
+// `need`-th largest key K* and returns it; *need_eq = how many entries equal to K* are taken.
 // *cnt_eq = how many entries equal K*.
+template <int NPL>
 __device__ uint32_t wave_radix_select(const uint32_t* key, const bool* valid, int need, int* hist,
                                       int* scratch, int* need_eq, int* cnt_eq) {
   const int l = threadIdx.x & 63;
@@ -83,7 +91,7 @@ __device__ uint32_t wave_radix_select(const uint32_t* key, const bool* valid, in
     for (int q = 0; q < 4; ++q) hist[4 * l + q] = 0;
     wave_sync();
 #pragma unroll
-    for (int u = 0; u < XPL; ++u)
+    for (int u = 0; u < NPL; ++u)
       if (valid[u] && (key[u] & pmask) == prefix) atomicAdd(&hist[(key[u] >> shift) & 255u], 1);
     wave_sync();
     int above;
@@ -97,60 +105,74 @@ __device__ uint32_t wave_radix_select(const uint32_t* key, const bool* valid, in
   return prefix;
 }
 
-// Reduce one row's buffer (cnt > E entries) to its E best entries under (score desc, token asc).
-__device__ float wave_compact_row(uint2* buf, int cnt, int E, int* hist, int* scratch) {
-  const int l = threadIdx.x & 63;
-  uint32_t key[XPL], tok[XPL];
-  bool valid[XPL];
+// Marks in keep[] the E best entries under (score desc, token asc) of NPL-per-lane entries
+// (all valid entries if there are at most E).  Returns the key of the E-th best (0 if fewer).
+template <int NPL>
+__device__ uint32_t wave_best(const uint32_t* key, const uint32_t* tok, const bool* valid, int cnt,
+                              int E, int* hist, int* scratch, bool* keep) {
+  if (cnt <= E) {
 #pragma unroll
-  for (int u = 0; u < XPL; ++u) {
-    const int p = l + 64 * u;
-    valid[u] = p < cnt;
-    uint2 e = valid[u] ? buf[p] : make_uint2(0u, 0u);
-    key[u] = float_key(__uint_as_float(e.x));
-    tok[u] = e.y;
+    for (int u = 0; u < NPL; ++u) keep[u] = valid[u];
+    return 0u;
   }
   int need_eq, cnt_eq;
-  const uint32_t kstar = wave_radix_select(key, valid, E, hist, scratch, &need_eq, &cnt_eq);
+  const uint32_t kstar = wave_radix_select<NPL>(key, valid, E, hist, scratch, &need_eq, &cnt_eq);
   uint32_t tmax = 0xFFFFFFFFu;   // largest token taken among those tying K*
   if (need_eq < cnt_eq) {
-    uint32_t k2[XPL];
-    bool v2[XPL];
+    uint32_t k2[NPL];
+    bool v2[NPL];
 #pragma unroll
-    for (int u = 0; u < XPL; ++u) {
+    for (int u = 0; u < NPL; ++u) {
       v2[u] = valid[u] && key[u] == kstar;
       k2[u] = ~tok[u];            // larger k2 = smaller token
     }
     int ne2, ce2;
-    const uint32_t t2 = wave_radix_select(k2, v2, need_eq, hist, scratch, &ne2, &ce2);
-    tmax = ~t2;
+    tmax = ~wave_radix_select<NPL>(k2, v2, need_eq, hist, scratch, &ne2, &ce2);
   }
-  bool keep[XPL];
 #pragma unroll
-  for (int u = 0; u < XPL; ++u)
+  for (int u = 0; u < NPL; ++u)
     keep[u] = valid[u] && (key[u] > kstar || (key[u] == kstar && tok[u] <= tmax));
+  return kstar;
+}
+
+// Cut one wave buffer (cnt > E entries) to its E best, in place; returns the E-th best key.
+__device__ uint32_t wave_cut(uint2* buf, int cnt, int E, int* hist, int* scratch) {
+  constexpr int NPL = EXTRA_CAP / 64;
+  const int l = threadIdx.x & 63;
+  uint32_t key[NPL], tok[NPL];
+  bool valid[NPL], keep[NPL];
+#pragma unroll
+  for (int u = 0; u < NPL; ++u) {
+    const int p = l + 64 * u;
+    valid[u] = p < cnt;
+    const uint2 e = valid[u] ? buf[p] : make_uint2(0u, 0u);
+    key[u] = float_key(__uint_as_float(e.x));
+    tok[u] = e.y;
+  }
+  const uint32_t kstar = wave_best<NPL>(key, tok, valid, cnt, E, hist, scratch, keep);
   // every lane holds its entries in registers now; write the survivors to the front
   int base = 0;
 #pragma unroll
-  for (int u = 0; u < XPL; ++u) {
+  for (int u = 0; u < NPL; ++u) {
     const uint64_t m = __ballot(keep[u]);
     const int pos = base + __popcll(m & ((1ull << l) - 1ull));
     if (keep[u]) buf[pos] = make_uint2(__float_as_uint(key_float(key[u])), tok[u]);
     base += __popcll(m);
   }
-  return key_float(kstar);
+  return kstar;
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void extra_select_kernel(Problem P) {
-  __shared__ float theta[XR];
-  __shared__ int cnt[XR];
+__global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P) {
+  __shared__ uint32_t thr[XR];            // shared threshold keys (0 = none yet)
   __shared__ int whist[4][256];
   __shared__ int wscr[4][4];
   __shared__ float qs[(sizeof(T) == 4) ? XR : 1][D];
 
-  const int bh = blockIdx.y, i0 = blockIdx.x * XR;
-  const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
+  const int bh = blockIdx.y, i0 = blockIdx.x * XR, slice = blockIdx.z;
+  const int S = P.extra_slices;
+  const int tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int rl = l % 32, i = i0 + rl;
   const int E = P.extra, N = P.N;
   const int b = bh / P.H, h = bh % P.H;
@@ -158,11 +180,10 @@ __global__ __launch_bounds__(256) void extra_select_kernel(Problem P) {
   const size_t grow = (size_t)bh * P.Mq + (i < P.Mq ? i : 0);
   const uint8_t* mrow = P.mult + grow * P.Mpad;
   const T* kbase = static_cast<const T*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)h * P.k.sh;
+  const int ts = (((N + S - 1) / S) + 127) / 128 * 128;       // tokens per slice
+  const int t_lo = slice * ts, t_hi = min(N, t_lo + ts);
 
-  if (tid < XR) {
-    theta[tid] = -__builtin_inff();
-    cnt[tid] = 0;
-  }
+  if (tid < XR) thr[tid] = 0u;
 
   // q̄ operands: split bf16 hi/lo fragments (bf16 inputs) or an fp32 copy in LDS
   bf16x8_t qhi[D / 16], qlo[D / 16];
@@ -173,8 +194,8 @@ __global__ __launch_bounds__(256) void extra_select_kernel(Problem P) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = (i < P.Mq) ? qb[16 * ks + 8 * (l / 32) + e] : 0.f;
-        const uint16_t hb = bf16_bits(x);
-        const uint16_t lb = bf16_bits(x - bf16_to_f32(hb));
+        const uint16_t hb = f32_to_bf16(x);
+        const uint16_t lb = f32_to_bf16(x - bf16_to_f32(hb));
         qhi[ks][e] = __builtin_bit_cast(__bf16, hb);
         qlo[ks][e] = __builtin_bit_cast(__bf16, lb);
       }
@@ -187,103 +208,218 @@ __global__ __launch_bounds__(256) void extra_select_kernel(Problem P) {
   }
   __syncthreads();
 
-  uint2* buf = P.extra_buf + grow * EXTRA_CAP;
-  for (int t0 = 0; t0 < N; t0 += XCHUNK) {
-    const int tw = t0 + 32 * w;
-    if (tw < N) {
-      float acc[16];
-      if constexpr (sizeof(T) == 2) {
-        f32x16_t c = {};
-        const T* kr = kbase + (int64_t)(tw + rl) * P.k.sn + 8 * (l / 32);
+  // candidate stores go through a buffer resource over this wave's buffers of the group's
+  // query blocks; a lane with nothing to store uses an offset past the end, which the buffer
+  // bounds check discards.  Every step issues the same number of stores, so waiting for the
+  // key prefetch never has to wait for them.
+  const uint32_t row_stride = (uint32_t)S * 4u * EXTRA_CAP * 8u;        // bytes between query blocks
+  const int nvalid = min(XR, P.Mq - i0);
+  const __amdgpu_buffer_rsrc_t brsrc =
+      xrsrc(P.extra_buf + (((size_t)bh * P.Mq + i0) * S + slice) * 4 * EXTRA_CAP + (size_t)w * EXTRA_CAP,
+            (uint32_t)(nvalid - 1) * row_stride + EXTRA_CAP * 8u);
+  const uint32_t my_off = (uint32_t)rl * row_stride;
+  // fill of this wave's buffer for the lane's query block; lanes l and l+32 share the block
+  // and keep the same count
+  int cnt = 0;
+  // bf16 path: the next step's key fragments and block flag are loaded one step ahead
+  bf16x8_t kf[D / 16];
+  uint8_t mnext = 0;
+  auto load_step = [&](int tw) {
+    if (tw < t_hi) {
+      const T* kr = kbase + (int64_t)(tw + rl) * P.k.sn + 8 * (l / 32);
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kr + 16 * ks);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qhi[ks], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qlo[ks], c, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = c[r];
-      } else {
+      for (int ks = 0; ks < D / 16; ++ks) kf[ks] = *reinterpret_cast<const bf16x8_t*>(kr + 16 * ks);
+      mnext = row_ok ? mrow[tw >> 6] : 0;
+    }
+  };
+  if constexpr (sizeof(T) == 2) load_step(t_lo + XSTEP * w);
 #pragma unroll 1
-        for (int r = 0; r < 16; ++r) {
-          const int tk = tw + (r / 4) * 8 + (l / 32) * 4 + (r % 4);
-          const float* kr = reinterpret_cast<const float*>(kbase) + (int64_t)tk * P.k.sn;
-          float s = 0.f;
+  for (int tw = t_lo + XSTEP * w; tw < t_hi; tw += 4 * XSTEP) {
+    float acc[16];
+    bool cand;
+    if constexpr (sizeof(T) == 2) {
+      bf16x8_t kc[D / 16];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) kc[ks] = kf[ks];
+      cand = mnext > 0;
+      load_step(tw + 4 * XSTEP);
+      f32x16_t c = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[ks], qhi[ks], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[ks], qlo[ks], c, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = c[r];
+    } else {
+#pragma unroll 1
+      for (int r = 0; r < 16; ++r) {
+        const int tk = tw + (r / 4) * 8 + (l / 32) * 4 + (r % 4);
+        const float* kr = reinterpret_cast<const float*>(kbase) + (int64_t)tk * P.k.sn;
+        float s = 0.f;
 #pragma unroll 8
-          for (int e = 0; e < D; ++e) s = fmaf(qs[rl][e], kr[e], s);
-          acc[r] = s;
-        }
+        for (int e = 0; e < D; ++e) s = fmaf(qs[rl][e], kr[e], s);
+        acc[r] = s;
       }
-      const bool cand = row_ok && mrow[tw / P.bk] > 0;
-      const float th = theta[rl];
-      if (cand) {
+      cand = row_ok && mrow[tw >> 6] > 0;
+    }
+    const uint32_t th = thr[rl];
+    uint32_t bits = 0;
+    if (cand) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (acc[r] > th) {
-            const int tk = tw + (r / 4) * 8 + (l / 32) * 4 + (r % 4);
-            const int pos = atomicAdd(&cnt[rl], 1);
-            buf[pos] = make_uint2(__float_as_uint(acc[r]), static_cast<uint32_t>(tk));
-          }
-        }
+      for (int r = 0; r < 16; ++r) bits |= (float_key(acc[r]) > th ? 1u : 0u) << r;
+    }
+    // append: lane l first, then its partner l+32, each in register order
+    const int mine = __popc(bits);
+    const int other = __shfl_xor(mine, 32);
+    const int pos0 = cnt + (l < 32 ? 0 : other);
+    cnt += mine + other;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tk = tw + (r / 4) * 8 + (l / 32) * 4 + (r % 4);
+      const uint32_t off = ((bits >> r) & 1u)
+                               ? my_off + (uint32_t)(pos0 + __popc(bits & ((1u << r) - 1u))) * 8u
+                               : 0xFFFFFFF0u;
+      u32x2 v2;
+      v2.x = __float_as_uint(acc[r]);
+      v2.y = static_cast<uint32_t>(tk);
+      __builtin_amdgcn_raw_buffer_store_b64(v2, brsrc, off, 0, 0);
+    }
+    // cut the buffers that the next step could overflow
+    uint64_t m = __ballot(l < 32 && cnt > EXTRA_CAP - XSTEP);
+    if (m) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this wave's stores, visible
+      while (m) {
+        const int rr = __builtin_ctzll(m);
+        m &= m - 1;
+        uint2* rb = P.extra_buf + ((((size_t)bh * P.Mq + i0 + rr) * S + slice) * 4 + w) * EXTRA_CAP;
+        const int crr = __shfl(cnt, rr);
+        const uint32_t kth = wave_cut(rb, crr, E, whist[w], wscr[w]);
+        if (l == 0) atomicMax(&thr[rr], kth);
+        if (rl == rr) cnt = E;
+        wave_sync();
       }
     }
-    __syncthreads();
-    // cut a buffer back to its E best entries when the next step could overflow it, and
-    // after the last step
-    const bool last = t0 + XCHUNK >= N;
-    for (int rr = w; rr < XR; rr += 4) {
-      const int c = cnt[rr];
-      if (c > EXTRA_CAP - XCHUNK || (last && c > E)) {
-        uint2* rb = P.extra_buf + ((size_t)bh * P.Mq + i0 + rr) * EXTRA_CAP;
-        const float th = wave_compact_row(rb, c, E, whist[w], wscr[w]);
-        if (l == 0) {
-          theta[rr] = th;
-          cnt[rr] = E;
-        }
-      }
-    }
-    __syncthreads();
   }
-
-  // rank the survivors by token, write them out, and take them out of their blocks' centroids
-  for (int rr = w; rr < XR; rr += 4) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  // publish the buffer fills; the merge pass takes the best E over all lists of a query block
+  for (int rr = 0; rr < XR; ++rr) {
     const int ii = i0 + rr;
-    if (ii >= P.Mq || (ii >= P.dense_q0 && ii < P.dense_q1)) continue;
+    if (ii >= P.Mq) break;
     const size_t row = (size_t)bh * P.Mq + ii;
-    const uint2* rb = P.extra_buf + row * EXTRA_CAP;
-    const int c = cnt[rr];
-    int* toks = whist[w];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = l + 64 * u;
-      if (p < c) toks[p] = static_cast<int>(rb[p].y);
-    }
-    wave_sync();
-    int* out = P.extra_idx + row * MAX_EXTRA;
-    uint8_t* mr = P.mult + row * P.Mpad;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = l + 64 * u;
-      if (p >= c) continue;
-      const int t = toks[p], bt = t / P.bk;
-      int rank = 0, same = 0, same_before = 0;
-      for (int q = 0; q < c; ++q) {
-        const int o = toks[q];
-        rank += o < t;
-        const bool sb = (o / P.bk) == bt;
-        same += sb;
-        same_before += sb && o < t;
-      }
-      out[rank] = t;
-      if (same_before == 0) mr[bt] = static_cast<uint8_t>(P.bk - same);
-    }
-    if (l == 0) P.extra_cnt[row] = c;
-    wave_sync();
+    const int c = __shfl(cnt, rr);
+    if (l == 0) P.extra_part[(row * S + slice) * 4 + w] = c;
   }
 }
 
+// Pass 2: best E of the 4*S partial lists of one query block, ranked by token.  The lists stay
+// in memory (L2-resident); each radix pass re-reads them.
+__global__ __launch_bounds__(64) void extra_merge_kernel(Problem P) {
+  __shared__ int hist[256];
+  __shared__ int scr[4];
+  __shared__ int toks[MAX_EXTRA];
+  const int i = blockIdx.x, bh = blockIdx.y, l = threadIdx.x;
+  const size_t row = (size_t)bh * P.Mq + i;
+  const int E = P.extra, S = P.extra_slices;
+  if (i >= P.dense_q0 && i < P.dense_q1) return;          // dense rows keep extra_cnt = 0
+  const int nl = 4 * S;
+  const int* part = P.extra_part + row * nl;
+  const uint2* lists = P.extra_buf + row * nl * EXTRA_CAP;
+  int cnts[16];
+  int total = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    cnts[q] = q < nl ? part[q] : 0;
+    total += cnts[q];
+  }
+  // visit every entry: list q, position p
+  auto for_each = [&](auto&& f) {
+#pragma unroll 1
+    for (int q = 0; q < nl; ++q) {
+      const uint2* lq = lists + q * EXTRA_CAP;
+      for (int p = l; p < cnts[q]; p += 64) f(lq[p]);
+    }
+  };
+  uint32_t kstar = 0, tmax = 0xFFFFFFFFu;
+  bool all = total <= E;
+  if (!all) {
+    // radix select of the E-th best key
+    uint32_t prefix = 0, pmask = 0;
+    int need = E, at = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hist[4 * l + q] = 0;
+      wave_sync();
+      for_each([&](uint2 e) {
+        const uint32_t k = float_key(__uint_as_float(e.x));
+        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+      });
+      wave_sync();
+      int above;
+      const int dg = wave_pick_digit(hist, need, &above, &at, scr);
+      prefix |= static_cast<uint32_t>(dg) << shift;
+      pmask |= 0xFFu << shift;
+      need -= above;
+    }
+    kstar = prefix;
+    if (need < at) {
+      // ties at K*: keep the `need` lowest tokens -> radix select on inverted tokens
+      uint32_t p2 = 0, m2 = 0;
+      int need2 = need, at2 = 0;
+      for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hist[4 * l + q] = 0;
+        wave_sync();
+        for_each([&](uint2 e) {
+          const uint32_t k = float_key(__uint_as_float(e.x));
+          const uint32_t k2 = ~e.y;
+          if (k == kstar && (k2 & m2) == p2) atomicAdd(&hist[(k2 >> shift) & 255u], 1);
+        });
+        wave_sync();
+        int above;
+        const int dg = wave_pick_digit(hist, need2, &above, &at2, scr);
+        p2 |= static_cast<uint32_t>(dg) << shift;
+        m2 |= 0xFFu << shift;
+        need2 -= above;
+      }
+      tmax = ~p2;
+    }
+  }
+  // survivors -> LDS (any order), then rank by token
+  if (l == 0) scr[3] = 0;
+  wave_sync();
+  for_each([&](uint2 e) {
+    const uint32_t k = float_key(__uint_as_float(e.x));
+    if (all || k > kstar || (k == kstar && e.y <= tmax)) toks[atomicAdd(&scr[3], 1)] = static_cast<int>(e.y);
+  });
+  wave_sync();
+  const int c = scr[3];
+  int* out = P.extra_idx + row * MAX_EXTRA;
+  uint8_t* mr = P.mult + row * P.Mpad;
+  for (int p = l; p < c; p += 64) {
+    const int t = toks[p], bt = t / P.bk;
+    int rank = 0, same = 0, same_before = 0;
+    for (int q = 0; q < c; ++q) {
+      const int o = toks[q];
+      rank += o < t;
+      const bool sb = (o / P.bk) == bt;
+      same += sb;
+      same_before += sb && o < t;
+    }
+    out[rank] = t;
+    if (same_before == 0) {
+      const int m = P.bk - same;
+      mr[bt] = static_cast<uint8_t>(m);
+      P.cbias[row * P.Mpad + bt] = m > 0 ? __logf(static_cast<float>(m)) / P.scale : -__builtin_inff();
+    }
+  }
+  if (l == 0) P.extra_cnt[row] = c;
+}
+
 hipError_t launch_extra_select(const Problem& P, hipStream_t stream) {
-  dim3 grid((P.Mq + XR - 1) / XR, P.B * P.H);
+  dim3 grid((P.Mq + XR - 1) / XR, P.B * P.H, P.extra_slices);
   if (P.dtype == 0) {
     if (P.d == 128) hipLaunchKernelGGL((extra_select_kernel<uint16_t, 128>), grid, dim3(256), 0, stream, P);
     else hipLaunchKernelGGL((extra_select_kernel<uint16_t, 64>), grid, dim3(256), 0, stream, P);
@@ -291,6 +427,10 @@ hipError_t launch_extra_select(const Problem& P, hipStream_t stream) {
     if (P.d == 128) hipLaunchKernelGGL((extra_select_kernel<float, 128>), grid, dim3(256), 0, stream, P);
     else hipLaunchKernelGGL((extra_select_kernel<float, 64>), grid, dim3(256), 0, stream, P);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2(P.Mq, P.B * P.H);
+  hipLaunchKernelGGL(extra_merge_kernel, g2, dim3(64), 0, stream, P);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ namespace solattn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -31,22 +32,35 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Asynchronous 16-byte global -> LDS copy: lane l's 16 bytes land at `wave_dst` + 16*l, where
-// `wave_dst` is the same for the whole wave.
-__device__ __forceinline__ void copy16_to_lds(const void* src, void* wave_dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(wave_dst), 16, 0, 0);
+// Asynchronous 16-byte global -> LDS copy through a buffer resource: lane l's 16 bytes land at
+// `wave_dst` + 16*l (the same `wave_dst` for the whole wave); `voff` is the lane's byte offset
+// from the resource base.  Out-of-range offsets read zero.
+__device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* wave_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(wave_dst), 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Double-buffered LDS tiles.  K: 64 keys x D, 16-byte chunks of each row XOR-swizzled by the row
-// index.  V: either the transposed tile (D rows of 64 keys, chunks swizzled by row) or, for
-// gathered extra tokens, plain row-major 64 x D.  Bias: per query block of the pair, per key.
+// LDS swizzles: the 16-byte chunk c of row r is stored at chunk position kswz/vswz(r, c), so that
+// any 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int kswz(int r, int c) {
+  if constexpr (D == 128) return c ^ (r & 15);        // 256-byte rows
+  else return c ^ ((r >> 1) & 7);                     // 128-byte rows
+}
+__device__ __forceinline__ int vswz(int r, int c) { return c ^ ((r >> 1) & 7); }   // 128-byte rows
+
+// Double-buffered LDS tiles.  K: 64 keys x D (chunk-swizzled rows).  V: transposed, D rows of 64
+// keys (chunk-swizzled).  Bias: per query block of the pair, per key (centroid and extra tiles).
 template <int D>
 struct FlashSmem {
-  uint16_t k[2][64 * D];
-  uint16_t v[2][64 * D];
-  float bias[2][2][64];
+  __attribute__((aligned(16))) uint16_t k[2][64 * D];
+  __attribute__((aligned(16))) uint16_t v[2][64 * D];
+  __attribute__((aligned(16))) float bias[2][2][64];
 };
 
 struct TileDesc {
@@ -86,7 +100,7 @@ struct TileIter {
 // heaviest) come first, then the rest head-major.  Consecutive units go to the same XCD in runs
 // of XCD_RUN (workgroups are dealt to the 8 XCDs round-robin), so one XCD works on neighbouring
 // query blocks of one head and shares their key tiles in its L2.
-constexpr int XCD_RUN = 16;
+constexpr int XCD_RUN = 64;
 
 __device__ __forceinline__ bool flash_unit(const Problem& P, int G, int gid, int* bh, int* pair) {
   const int x = gid % 8, k = gid / 8;
@@ -120,6 +134,7 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
   constexpr int KCH = D / 8;                 // 16-byte chunks per K row
   constexpr int SLOTS = 64 * D / 8;          // 16-byte slots per tile matrix
   constexpr int PER_THREAD = SLOTS / 256;
+  constexpr int TILE_BYTES = 64 * D * 2;
   int bh, pair;
   if (!flash_unit(P, G, blockIdx.x, &bh, &pair)) return;
   const int tid = threadIdx.x, w = tid / 64, l = tid % 64, h32 = l / 32, c32 = l % 32;
@@ -134,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
   bool dense[2], valid[2];
   const int* klist[2];
   const int* elist[2];
-  const uint8_t* mrow[2];
+  const float* cbrow[2];
 #pragma unroll
   for (int gg = 0; gg < 2; ++gg) {
     qb[gg] = pair * G + gg;
@@ -146,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
     ne[gg] = (valid[gg] && !dense[gg]) ? uniform(P.extra_cnt[row]) : 0;
     klist[gg] = P.kept_idx + row * P.M;
     elist[gg] = P.extra_idx + row * MAX_EXTRA;
-    mrow[gg] = P.mult + row * P.Mpad;
+    cbrow[gg] = P.cbias + row * P.Mpad;
   }
   int cent_sel = 0;
   if (P.mode == 0) {
@@ -166,42 +181,52 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * ks);
   }
 
-  // ---- issue the asynchronous loads of one tile into buffer bf.  Sources are a uniform base
-  // pointer plus a 32-bit per-lane byte offset (row strides are bounded on the host).
+  // per-lane byte offsets of the tile loads (slot s of this lane in instruction u):
+  // K row r = s / KCH, chunk c = s % KCH, stored at swizzled chunk kswz(r, c);
+  // transposed V row vr = s / 8, chunk vc = s % 8, stored at vswz(vr, vc).
   const uint32_t ksn_b = static_cast<uint32_t>(P.k.sn) * 2u;
   const uint32_t vsn_b = static_cast<uint32_t>(P.v.sn) * 2u;
+  uint32_t krow[PER_THREAD], kcol[PER_THREAD], voff[PER_THREAD];
+#pragma unroll
+  for (int u = 0; u < PER_THREAD; ++u) {
+    const int s = (u * 4 + w) * 64 + l;
+    const int r = s / KCH, c = s % KCH;
+    krow[u] = r;
+    kcol[u] = kswz<D>(r, c) * 16;
+    const int vr = s / 8, vc = s % 8;
+    voff[u] = vr * 128 + vswz(vr, vc) * 16;
+  }
+
+  // ---- issue the asynchronous loads of one tile into buffer bf
   auto issue = [&](const TileDesc& t, int bf) {
-    uint16_t* kd = sm.k[bf];
-    uint16_t* vd = sm.v[bf];
-    const char* kbase;
+    char* kd = reinterpret_cast<char*>(sm.k[bf]) + w * 1024;
+    char* vd = reinterpret_cast<char*>(sm.v[bf]) + w * 1024;
+    const void* kbase;
     uint32_t krow_b;
-    const char* vbase;
+    const void* vbase;
     if (t.kind == 0) {
-      kbase = reinterpret_cast<const char*>(Kb + (int64_t)t.idx * 64 * P.k.sn);
+      kbase = Kb + (int64_t)t.idx * 64 * P.k.sn;
       krow_b = ksn_b;
-      vbase = reinterpret_cast<const char*>(P.v_t + ((size_t)bh * P.M + t.idx) * D * 64);
+      vbase = P.v_t + ((size_t)bh * P.M + t.idx) * D * 64;
     } else {
-      kbase = reinterpret_cast<const char*>(P.kbar_bf + ((size_t)bh * P.Mpad + t.idx) * D);
+      kbase = P.kbar_bf + ((size_t)bh * P.Mpad + t.idx) * D;
       krow_b = D * 2;
-      vbase = reinterpret_cast<const char*>(P.vbar_t + ((size_t)bh * (P.Mpad / 64) + t.idx / 64) * D * 64);
+      vbase = P.vbar_t + ((size_t)bh * (P.Mpad / 64) + t.idx / 64) * D * 64;
     }
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, 64u * krow_b);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, TILE_BYTES);
 #pragma unroll
     for (int u = 0; u < PER_THREAD; ++u) {
-      const int s = (u * 4 + w) * 64 + l;
-      const int r = s / KCH, c = s % KCH;
-      copy16_to_lds(kbase + (uint32_t)r * krow_b + (uint32_t)((c ^ (r & (KCH - 1))) * 16),
-                    kd + (u * 4 + w) * 64 * 8);
-      const int vr = s / 8, vc = s % 8;
-      copy16_to_lds(vbase + (uint32_t)(vr * 128 + (vc ^ (vr & 7)) * 16), vd + (u * 4 + w) * 64 * 8);
+      buf_to_lds16(kr, krow[u] * krow_b + kcol[u], kd + u * 4096);
+      buf_to_lds16(vr, voff[u], vd + u * 4096);
     }
-    if (t.kind == 2 && tid < 128) {
-      const int gg = tid / 64, key = tid % 64;
-      float bv = -__builtin_inff();
-      if ((t.sel >> gg) & 1) {
-        const int m = mrow[gg][t.idx + key];   // 0: kept block or padding beyond M
-        bv = m > 0 ? __log2f(static_cast<float>(m)) : -__builtin_inff();
+    if (t.kind == 2 && w == 0) {
+      // both query blocks' 64 biases: lanes 0-15 block 0, lanes 16-31 block 1
+      const int gg = l >> 4;
+      if (l < 32) {
+        const __amdgpu_buffer_rsrc_t br = make_rsrc(cbrow[gg] + t.idx, 256);
+        buf_to_lds16(br, (l & 15) * 16, reinterpret_cast<char*>(sm.bias[bf]));
       }
-      sm.bias[bf][gg][key] = bv;
     }
   };
 
@@ -211,78 +236,125 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
   float m_run = -__builtin_inff();
   float l_run = 0.f;
   const float sl2 = P.scale * LOG2E;
+  // LDS read offsets: chunk (2ks + h32) of row r sits at byte ((32ks) ^ Y) within the row, with Y
+  // a lane constant, so each read is one XOR with a compile-time constant.
+  const uint32_t ak = c32 * (D * 2) + 16 * (kswz<D>(c32, 0) ^ h32);
+  const uint32_t av = c32 * 128 + 16 * (vswz(c32, 0) ^ h32);
+  const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
   // ---- one tile for this wave's 32 query rows
   auto compute = [&](const TileDesc& t, int bf) {
-    const uint16_t* kt_ = sm.k[bf];
-    const uint16_t* vt_ = sm.v[bf];
+    const char* kt_ = reinterpret_cast<const char*>(sm.k[bf]);
+    const char* vt_ = reinterpret_cast<const char*>(sm.v[bf]);
+    // S^T = K Q^T; the K fragments of step ks+1 are read while step ks multiplies
     f32x16_t s[2];
+    s[0] = f32x16_t{};
+    s[1] = f32x16_t{};
+    bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kt_ + ak);
+    bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kt_ + ak + 32 * D * 2);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16_t{};
-      const int r = 32 * kt + c32;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const int c = (2 * ks + h32) ^ (r & (KCH - 1));
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt_ + r * D + c * 8);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
+    for (int ks = 0; ks < D / 16; ++ks) {
+      bf16x8_t n0 = a0, n1 = a1;
+      if (ks + 1 < D / 16) {
+        const uint32_t off = ak ^ (32u * (ks + 1));
+        n0 = *reinterpret_cast<const bf16x8_t*>(kt_ + off);
+        n1 = *reinterpret_cast<const bf16x8_t*>(kt_ + off + 32 * D * 2);
       }
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s[1], 0, 0, 0);
+      a0 = n0;
+      a1 = n1;
     }
-    // register r of half kt holds key 32kt + (r/4)*8 + 4*h32 + r%4
-    float mx = -__builtin_inff();
-    if (t.kind == 0) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[kt][r] *= sl2;
-          mx = fmaxf(mx, s[kt][r]);
-        }
-    } else {   // centroid and extra-token tiles carry a per-key bias
+    __builtin_amdgcn_s_setprio(0);
+    // register r of half kt holds key 32kt + (r/4)*8 + 4*h32 + r%4.  Centroid and extra tiles
+    // add their per-key bias, kept in raw-score units (ln(m) * sqrt(d), or -inf), in place.
+    if (t.kind != 0) {
       const float* bias = sm.bias[bf][g];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kt + (r / 4) * 8 + 4 * h32 + (r % 4);
-          s[kt][r] = fmaf(s[kt][r], sl2, bias[key]);
-          mx = fmaxf(mx, s[kt][r]);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 bv = *reinterpret_cast<const float4*>(bias + 32 * kt + r4 * 8 + 4 * h32);
+          s[kt][4 * r4 + 0] += bv.x;
+          s[kt][4 * r4 + 1] += bv.y;
+          s[kt][4 * r4 + 2] += bv.z;
+          s[kt][4 * r4 + 3] += bv.w;
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float psum = 0.f;
+    // base-2 logits x = s * scale * log2(e); the max is taken on s (the scale is positive)
+    float mx = -__builtin_inff();
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[kt][r] - m_use);
-        psum += p;
-        s[kt][r] = p;
-      }
-    l_run = fmaf(l_run, alpha, psum);
-    m_run = m_new;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    mx *= sl2;
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // Lazy rescaling: the reference max moves (and the accumulator is rescaled) only when some
+    // row's max grows by more than 8 (base 2), so probabilities stay below 2^8 and most tiles
+    // skip the rescale.  The result is the same softmax, referenced to a different constant.
+    const float m_cand = fmaxf(m_run, mx);
+    if (__any(m_cand > m_run + 8.f)) {
+      const float m_new = m_cand == -__builtin_inff() ? m_run : m_cand;
+      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    // O^T += V^T P^T, one 16-key step at a time: P^T for keys 16ks.. is registers
-    // 8(ks%2)..+8 of score half ks/2
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = m_run == -__builtin_inff() ? 0.f : -m_run;
+    // O^T += V^T P^T, one 16-key step at a time.  The probabilities of step ks (registers
+    // 8(ks%2)..+8 of score half ks/2) are rounded to bf16 and summed (the sum sees the rounded
+    // values, as the product does).  Software pipeline: while the four products of step ks run
+    // on the matrix unit, the exponentials of step ks+1 run on the vector unit.
+    float psum = 0.f;
+    auto probs = [&](int ks) {
       bf16x8_t pf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = static_cast<__bf16>(s[ks / 2][8 * (ks % 2) + e]);
+      for (int e = 0; e < 8; ++e)
+        pf[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[ks / 2][8 * (ks % 2) + e], sl2, nm)));
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const int r = 32 * dt + c32;
-        const int c = (2 * ks + h32) ^ (r & 7);
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vt_ + r * 64 + c * 8);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, o[dt], 0, 0, 0);
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2_t pp = {pf[2 * e], pf[2 * e + 1]};
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
+      }
+      return pf;
+    };
+    bf16x8_t va[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      va[dt] = *reinterpret_cast<const bf16x8_t*>(vt_ + av + dt * 32 * 128);
+    bf16x8_t pcur = probs(0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t vn[D / 32];
+      bf16x8_t pnext = pcur;
+      if (ks + 1 < 4) {
+        const uint32_t off = av ^ (32u * (ks + 1));
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          vn[dt] = *reinterpret_cast<const bf16x8_t*>(vt_ + off + dt * 32 * 128);
+        pnext = probs(ks + 1);
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], pcur, o[dt], 0, 0, 0);
+      if (ks + 1 < 4) {
+        // one product, then a slice of the next step's vector work, four times
+        __builtin_amdgcn_sched_group_barrier(0x100, D / 32, 0);    // LDS reads of step ks+1
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x406, 7, 0);      // VALU incl. exp
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) va[dt] = vn[dt];
+        pcur = pnext;
       }
     }
+    l_run += psum;
   };
 
   TileDesc cur = it.next();
@@ -317,8 +389,9 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
         const int r = sl / KCH, c = sl % KCH;
         const int e = e0 + r < cnt ? e0 + r : e0;               // padding rows reuse a real token
         const uint32_t tok = static_cast<uint32_t>(el[e]);
-        copy16_to_lds(reinterpret_cast<const char*>(Kb) + (size_t)tok * ksn_b + ((c ^ (r & (KCH - 1))) * 16),
-                      kd + (u * 4 + w) * 64 * 8);
+        const uint4 kv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Kb) +
+                                                         (size_t)tok * ksn_b + c * 16);
+        *reinterpret_cast<uint4*>(kd + r * D + kswz<D>(r, c) * 8) = kv;
         const uint4 vv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Vb) +
                                                          (size_t)tok * vsn_b + c * 16);
         const uint16_t* vx = reinterpret_cast<const uint16_t*>(&vv);
@@ -326,11 +399,10 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const int dr = c * 8 + x;                           // d row of the transposed tile
-          vd[dr * 64 + (((pos >> 3) ^ (dr & 7)) << 3) + (pos & 7)] = vx[x];
+          vd[dr * 64 + (vswz(dr, pos >> 3) << 3) + (pos & 7)] = vx[x];
         }
       }
       if (tid < 64) sm.bias[0][gg][tid] = e0 + tid < cnt ? 0.f : -__builtin_inff();
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (wave_on && g == gg) compute(TileDesc{1, e0, 1 << gg}, 0);
     }
@@ -353,8 +425,6 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
       *reinterpret_cast<bf16x4_t*>(Ob + d0) = pk;
     }
 }
-
-// ------------------------------------------------------------------ fp32 path
 
 // fp32 path: workgroup -> (head, query block), dense query blocks (the heaviest) first.
 __device__ __forceinline__ void flash_work(const Problem& P, int g, int* bh, int* qi) {

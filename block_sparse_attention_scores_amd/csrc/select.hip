@@ -58,12 +58,16 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
   const float* s = P.scores + row * M;
   int* kidx = P.kept_idx + row * M;
   uint8_t* mult = P.mult + row * P.Mpad;
+  float* cb = P.cbias + row * P.Mpad;
+  // centroid logit offset in raw-score units: ln(block size) / scale
+  const float log2_bk = __logf(static_cast<float>(P.bk)) / P.scale;
 
   const bool dense = i >= P.dense_q0 && i < P.dense_q1;
   if (dense || (P.mode == 0 && P.keep_all)) {
     for (int j = tid; j < P.Mpad; j += 256) {
       if (j < M) kidx[j] = j;
       mult[j] = 0;
+      cb[j] = -__builtin_inff();
     }
     if (tid == 0) {
       P.kept_cnt[row] = M;
@@ -154,10 +158,16 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
     int tot;
     const int pos = block_scan_incl(keep ? 1 : 0, ish, &tot) - (keep ? 1 : 0) + base;
     if (keep) kidx[pos] = j;
-    if (j < M) mult[j] = keep ? 0 : static_cast<uint8_t>(P.bk);
+    if (j < M) {
+      mult[j] = keep ? 0 : static_cast<uint8_t>(P.bk);
+      cb[j] = keep ? -__builtin_inff() : log2_bk;
+    }
     base += tot;
   }
-  for (int j = M + tid; j < P.Mpad; j += 256) mult[j] = 0;
+  for (int j = M + tid; j < P.Mpad; j += 256) {
+    mult[j] = 0;
+    cb[j] = -__builtin_inff();
+  }
   if (tid == 0) {
     P.kept_cnt[row] = base;
     P.extra_cnt[row] = 0;

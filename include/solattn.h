@@ -124,17 +124,20 @@ int solattn_check_args(int mode, const void* q, const void* k, const void* v, vo
  *   kept_cnt  int32 [B*H, Mq]      number of kept key blocks (M for dense query blocks)
  *   kept_idx  int32 [B*H, Mq, M]   kept key-block indices, ascending, first kept_cnt valid
  *   mult      uint8 [B*H, Mq, Mpad] centroid multiplicity of each key block (0 = attended exactly)
+ *   cbias     fp32 [B*H, Mq, Mpad] ln(multiplicity) * sqrt(d): the centroid term's logit offset
+ *             in raw q.k units, -inf where the multiplicity is 0
  *   extra_cnt int32 [B*H, Mq]      number of extra tokens
  *   extra_idx int32 [B*H, Mq, 256] extra token indices, ascending, first extra_cnt valid
- *   extra_buf 8-byte entries [B*H, Mq, 768]: scratch of the extra-token selection
+ *   extra_buf, extra_part: scratch of the extra-token selection (candidate lists per query
+ *             block, token slice and wave, and their lengths)
  *   kbar_bf   bf16 [B*H, Mpad, d], vbar_t bf16 [B*H, Mpad/64, d, 64], v_t bf16
  *             [B*H, M, d, 64]: operand copies for the attention kernel (bf16 only)
  * Mq = N/block_q, M = N/block_k, Mpad = M rounded up to a multiple of 64.
  */
 typedef struct solattn_ws_layout {
   size_t total;
-  size_t qbar, kbar, vbar, scores, kept_cnt, kept_idx, mult, extra_cnt, extra_idx;
-  size_t extra_buf;             /* candidate buffers of the extra-token selection          */
+  size_t qbar, kbar, vbar, scores, kept_cnt, kept_idx, mult, cbias, extra_cnt, extra_idx;
+  size_t extra_buf, extra_part;  /* scratch of the extra-token selection                   */
   size_t kbar_bf, vbar_t, v_t;
   int Mq, M, Mpad;
 } solattn_ws_layout;
