@@ -45,7 +45,7 @@ class Opts(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "total", "qbar", "kbar", "vbar", "scores", "kept_cnt", "kept_idx", "mult", "cbias", "extra_cnt",
+        "total", "qbar", "kbar", "vbar", "scores", "kept_cnt", "kept_idx", "kept_bm", "mult", "cbias", "extra_cnt",
         "extra_idx", "extra_buf", "extra_part", "kbar_bf", "vbar_t", "v_t")] + [
         ("Mq", ctypes.c_int), ("M", ctypes.c_int), ("Mpad", ctypes.c_int)]
 
@@ -241,6 +241,7 @@ def selection_views(workspace, mode, dtype, B, H, N, d, block_q, block_k):
         scores=view(L.scores, BH * Mq * M, torch.float32, (BH, Mq, M)),
         kept_cnt=view(L.kept_cnt, BH * Mq, torch.int32, (BH, Mq)),
         kept_idx=view(L.kept_idx, BH * Mq * M, torch.int32, (BH, Mq, M)),
+        kept_bm=view(L.kept_bm, BH * Mq * (Mpad // 64), torch.int64, (BH, Mq, Mpad // 64)),
         mult=view(L.mult, BH * Mq * Mpad, torch.uint8, (BH, Mq, Mpad)),
         cbias=view(L.cbias, BH * Mq * Mpad, torch.float32, (BH, Mq, Mpad)),
         extra_cnt=view(L.extra_cnt, BH * Mq, torch.int32, (BH, Mq)),

@@ -98,6 +98,8 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   if (N % block_q || N % block_k) return fail(SOLATTN_ENOTSUP, "N=%d not a multiple of the block sizes", N);
   if (d0 % block_q || d1 % block_q) return fail(SOLATTN_ENOTSUP, "dense rows not block_q aligned");
   if ((int64_t)B * H > 65535) return fail(SOLATTN_ENOTSUP, "B*H=%lld too large", (long long)B * H);
+  if (dtype == SOLATTN_BF16 && N / block_k > solattn::MAX_BLOCKS_BF16)
+    return fail(SOLATTN_ENOTSUP, "bf16: more than %d key blocks", solattn::MAX_BLOCKS_BF16);
   for (int t = 0; t < 4; ++t)   // the kernels address up to 64 rows with 32-bit byte offsets
     if (st[t].sn >= (int64_t(1) << 24)) return fail(SOLATTN_ENOTSUP, "row stride of %c too large", "qkvo"[t]);
   for (int t = 0; t < 4; ++t) {
@@ -130,6 +132,7 @@ int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int blo
   L->scores = take(BH * Mq * M * 4);
   L->kept_cnt = take(BH * Mq * 4);
   L->kept_idx = take(BH * Mq * M * 4);
+  L->kept_bm = take(BH * Mq * (Mpad / 64) * 8);
   L->mult = take(BH * Mq * Mpad);
   L->cbias = take(BH * Mq * Mpad * 4);
   L->extra_cnt = take(BH * Mq * 4);
@@ -246,6 +249,7 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   P.scores = reinterpret_cast<float*>(ws + L.scores);
   P.kept_cnt = reinterpret_cast<int*>(ws + L.kept_cnt);
   P.kept_idx = reinterpret_cast<int*>(ws + L.kept_idx);
+  P.kept_bm = reinterpret_cast<uint64_t*>(ws + L.kept_bm);
   P.mult = reinterpret_cast<uint8_t*>(ws + L.mult);
   P.cbias = reinterpret_cast<float*>(ws + L.cbias);
   P.extra_cnt = reinterpret_cast<int*>(ws + L.extra_cnt);

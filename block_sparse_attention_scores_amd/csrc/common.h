@@ -34,6 +34,7 @@ struct Problem {
   float* scores;
   int* kept_cnt;
   int* kept_idx;
+  uint64_t* kept_bm;     // kept blocks as a bitmap: word j/64, bit j%64
   uint8_t* mult;
   float* cbias;          // ln(centroid multiplicity) / scale (a raw-score offset), -inf where it is 0
   int* extra_cnt;
@@ -47,6 +48,8 @@ struct Problem {
 };
 
 constexpr int MAX_EXTRA = 256;
+// The bf16 attention kernel holds a query block's kept-block bitmap in one 64-bit word per lane.
+constexpr int MAX_BLOCKS_BF16 = 64 * 64;
 // Candidate buffer per (query block, token slice, wave) of the extra-token selection.  It is cut
 // back to the best extra_tokens entries only when one more 32-token step could overflow it,
 // which for the workloads here almost never happens.

@@ -69,23 +69,30 @@ struct TileDesc {
   int sel;    // bit g: query block g of the pair attends this tile
 };
 
-// Walks the pipelined work of a pair of query blocks: the union of their kept-block lists
-// (merged in ascending order), then the centroid tiles.  Every thread holds identical state, so
-// all decisions are uniform.  (Extra tokens are gathered in a separate pass afterwards.)
+__device__ __forceinline__ uint64_t readlane64(uint64_t x, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(x), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(x >> 32), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Walks the pipelined work of a pair of query blocks: every key block kept by either of them,
+// in ascending order, then the centroid tiles.  The two kept-block bitmaps are held one 64-bit
+// word per lane (lane l: blocks 64l..64l+63), so finding the next tile is a ballot and a few
+// lane reads, with no memory access.  Every decision is uniform across the wave.
 struct TileIter {
-  const int* list0;
-  const int* list1;
-  int n0, n1, p0, p1;
+  uint64_t w0, w1;   // this lane's words of the two bitmaps
+  uint64_t rem;      // bits of w0 | w1 not visited yet
   int pos, ncent, cent_sel;
   __device__ TileDesc next() {
-    const int a = p0 < n0 ? uniform(list0[p0]) : 0x7fffffff;
-    const int b = p1 < n1 ? uniform(list1[p1]) : 0x7fffffff;
-    if (a != 0x7fffffff || b != 0x7fffffff) {
-      const int j = a < b ? a : b;
-      const int sel = (a == j ? 1 : 0) | (b == j ? 2 : 0);
-      p0 += a == j;
-      p1 += b == j;
-      return TileDesc{0, j, sel};
+    const uint64_t act = __ballot(rem != 0);
+    if (act) {
+      const int L = static_cast<int>(__builtin_ctzll(act));
+      const uint64_t word = readlane64(rem, L);
+      const int bit = static_cast<int>(__builtin_ctzll(word));
+      const uint64_t a = readlane64(w0, L), b = readlane64(w1, L);
+      if (static_cast<int>(threadIdx.x & 63) == L) rem &= rem - 1;   // the lowest bit is `bit`
+      const int sel = static_cast<int>((a >> bit) & 1u) | (static_cast<int>((b >> bit) & 1u) << 1);
+      return TileDesc{0, 64 * L + bit, sel};
     }
     if (pos < ncent) {
       const int c = pos;
@@ -147,9 +154,8 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
   // per query block of the pair
   int qb[2], nk[2], ne[2];
   bool dense[2], valid[2];
-  const int* klist[2];
+  uint64_t kw[2];
   const int* elist[2];
-  const float* cbrow[2];
 #pragma unroll
   for (int gg = 0; gg < 2; ++gg) {
     qb[gg] = pair * G + gg;
@@ -159,17 +165,18 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
     dense[gg] = qq >= P.dense_q0 && qq < P.dense_q1;
     nk[gg] = valid[gg] ? uniform(P.kept_cnt[row]) : 0;
     ne[gg] = (valid[gg] && !dense[gg]) ? uniform(P.extra_cnt[row]) : 0;
-    klist[gg] = P.kept_idx + row * P.M;
+    const int nwords = P.Mpad / 64;
+    kw[gg] = (valid[gg] && l < nwords) ? P.kept_bm[row * nwords + l] : 0ull;
     elist[gg] = P.extra_idx + row * MAX_EXTRA;
-    cbrow[gg] = P.cbias + row * P.Mpad;
   }
+  const float* cbrow0 = P.cbias + ((size_t)bh * P.Mq + pair * G) * P.Mpad;
   int cent_sel = 0;
   if (P.mode == 0) {
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg)
       if (valid[gg] && !dense[gg] && nk[gg] < P.M) cent_sel |= 1 << gg;
   }
-  TileIter it{klist[0], klist[1], nk[0], nk[1], 0, 0, 0, cent_sel ? P.Mpad : 0, cent_sel};
+  TileIter it{kw[0], kw[1], kw[0] | kw[1], 0, cent_sel ? P.Mpad : 0, cent_sel};
 
   // this wave's 32 query rows: Q^T operand fragments
   const bool wave_on = valid[g];
@@ -220,13 +227,13 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
       buf_to_lds16(kr, krow[u] * krow_b + kcol[u], kd + u * 4096);
       buf_to_lds16(vr, voff[u], vd + u * 4096);
     }
-    if (t.kind == 2 && w == 0) {
-      // both query blocks' 64 biases: lanes 0-15 block 0, lanes 16-31 block 1
-      const int gg = l >> 4;
-      if (l < 32) {
-        const __amdgpu_buffer_rsrc_t br = make_rsrc(cbrow[gg] + t.idx, 256);
-        buf_to_lds16(br, (l & 15) * 16, reinterpret_cast<char*>(sm.bias[bf]));
-      }
+    if (t.kind == 2 && w == 0 && l < 32) {
+      // the 64 biases of both query blocks (consecutive rows): lanes 0-15 block 0, 16-31 block 1
+      const uint32_t nrec = static_cast<uint32_t>(
+          uniform((G == 2 && valid[1]) ? P.Mpad * 4 + 256 : 256));
+      const __amdgpu_buffer_rsrc_t br = make_rsrc(cbrow0 + t.idx, nrec);
+      buf_to_lds16(br, static_cast<uint32_t>(l >> 4) * static_cast<uint32_t>(P.Mpad) * 4u + (l & 15) * 16,
+                   reinterpret_cast<char*>(sm.bias[bf]));
     }
   };
 
@@ -242,14 +249,28 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
   const uint32_t av = c32 * 128 + 16 * (vswz(c32, 0) ^ h32);
   const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
-  // ---- one tile for this wave's 32 query rows
-  auto compute = [&](const TileDesc& t, int bf) {
+  // The score accumulators of a tile start from its per-key bias (centroid and extra tiles:
+  // ln(m) * sqrt(d) in raw-score units, or -inf; kept tiles: 0).  Register r of half kt holds
+  // key 32kt + (r/4)*8 + 4*h32 + r%4.  The bias is read from LDS before the next tile's
+  // asynchronous copies are issued, so the read never has to wait for them.
+  auto load_bias = [&](const float* bias, f32x16_t* s) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 bv = *reinterpret_cast<const float4*>(bias + 32 * kt + r4 * 8 + 4 * h32);
+        s[kt][4 * r4 + 0] = bv.x;
+        s[kt][4 * r4 + 1] = bv.y;
+        s[kt][4 * r4 + 2] = bv.z;
+        s[kt][4 * r4 + 3] = bv.w;
+      }
+  };
+
+  // ---- one tile for this wave's 32 query rows; s holds the initial accumulators
+  auto compute = [&](int bf, f32x16_t* s) {
     const char* kt_ = reinterpret_cast<const char*>(sm.k[bf]);
     const char* vt_ = reinterpret_cast<const char*>(sm.v[bf]);
-    // S^T = K Q^T; the K fragments of step ks+1 are read while step ks multiplies
-    f32x16_t s[2];
-    s[0] = f32x16_t{};
-    s[1] = f32x16_t{};
+    // S^T = K Q^T (+ bias); the K fragments of step ks+1 are read while step ks multiplies
     bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kt_ + ak);
     bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kt_ + ak + 32 * D * 2);
     __builtin_amdgcn_s_setprio(1);
@@ -267,21 +288,6 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
       a1 = n1;
     }
     __builtin_amdgcn_s_setprio(0);
-    // register r of half kt holds key 32kt + (r/4)*8 + 4*h32 + r%4.  Centroid and extra tiles
-    // add their per-key bias, kept in raw-score units (ln(m) * sqrt(d), or -inf), in place.
-    if (t.kind != 0) {
-      const float* bias = sm.bias[bf][g];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const float4 bv = *reinterpret_cast<const float4*>(bias + 32 * kt + r4 * 8 + 4 * h32);
-          s[kt][4 * r4 + 0] += bv.x;
-          s[kt][4 * r4 + 1] += bv.y;
-          s[kt][4 * r4 + 2] += bv.z;
-          s[kt][4 * r4 + 3] += bv.w;
-        }
-    }
     // base-2 logits x = s * scale * log2(e); the max is taken on s (the scale is positive)
     float mx = -__builtin_inff();
 #pragma unroll
@@ -363,9 +369,14 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
   for (;;) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    const bool mine = wave_on && ((cur.sel >> g) & 1);
+    f32x16_t s[2];
+    s[0] = f32x16_t{};
+    s[1] = f32x16_t{};
+    if (mine && cur.kind != 0) load_bias(sm.bias[bf][g], s);
     const TileDesc nxt = it.next();
     if (nxt.kind != 3) issue(nxt, bf ^ 1);
-    if (wave_on && ((cur.sel >> g) & 1)) compute(cur, bf);
+    if (mine) compute(bf, s);
     if (nxt.kind == 3) break;
     cur = nxt;
     bf ^= 1;
@@ -404,7 +415,11 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
       }
       if (tid < 64) sm.bias[0][gg][tid] = e0 + tid < cnt ? 0.f : -__builtin_inff();
       __syncthreads();
-      if (wave_on && g == gg) compute(TileDesc{1, e0, 1 << gg}, 0);
+      if (wave_on && g == gg) {
+        f32x16_t s[2];
+        load_bias(sm.bias[0][gg], s);
+        compute(0, s);
+      }
     }
   }
 

@@ -6,6 +6,8 @@
 //     ties to the lower index (radix select on order-preserving keys).
 //   Sink blocks and the diagonal block(s) are kept on top in both modes (node docs, sla
 //   table, and sink_conditioning row).  Query blocks in the dense row range keep every block.
+// The kept set is written twice: as an ascending index list and as a bitmap (bit j of word
+// j/64), which the attention kernel walks without touching memory.
 // One 256-thread workgroup per row; all reductions have a fixed order, so results are
 // deterministic.  Also writes each block's centroid multiplicity (0 = attended exactly).
 #include "common.h"
@@ -59,6 +61,8 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
   int* kidx = P.kept_idx + row * M;
   uint8_t* mult = P.mult + row * P.Mpad;
   float* cb = P.cbias + row * P.Mpad;
+  uint64_t* bm = P.kept_bm + row * (P.Mpad / 64);
+  const int lane = tid & 63, wv = tid >> 6;
   // centroid logit offset in raw-score units: ln(block size) / scale
   const float log2_bk = __logf(static_cast<float>(P.bk)) / P.scale;
 
@@ -68,6 +72,10 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
       if (j < M) kidx[j] = j;
       mult[j] = 0;
       cb[j] = -__builtin_inff();
+    }
+    for (int wd = tid; wd < P.Mpad / 64; wd += 256) {
+      const int nb = M - 64 * wd;       // blocks of this word that exist
+      bm[wd] = nb >= 64 ? ~0ull : ((1ull << nb) - 1ull);
     }
     if (tid == 0) {
       P.kept_cnt[row] = M;
@@ -158,6 +166,9 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
     int tot;
     const int pos = block_scan_incl(keep ? 1 : 0, ish, &tot) - (keep ? 1 : 0) + base;
     if (keep) kidx[pos] = j;
+    const uint64_t word = __ballot(keep);
+    const int wd = (j0 >> 6) + wv;
+    if (lane == 0 && wd < P.Mpad / 64) bm[wd] = word;
     if (j < M) {
       mult[j] = keep ? 0 : static_cast<uint8_t>(P.bk);
       cb[j] = keep ? -__builtin_inff() : log2_bk;

@@ -79,7 +79,8 @@ typedef struct solattn_opts {
  *   out       device pointer, same shape and type, fully overwritten; must not
  *             overlap q, k or v.
  *   B, H, N, d  sizes (>= 1).  This build: d in {64, 128}, N % block_q == 0,
- *             N % block_k == 0.
+ *             N % block_k == 0, and for bf16 at most 4096 key blocks (N <= 262144
+ *             at block_k 64); other shapes return SOLATTN_ENOTSUP.
  *   tau       threshold in standard deviations of the row's block scores; any
  *             value but NaN.  -inf keeps every block (dense attention).
  *   block_q   query block size: 64 or 128.   block_k: key block size: 64.
@@ -123,6 +124,7 @@ int solattn_check_args(int mode, const void* q, const void* k, const void* v, vo
  *   scores    fp32 [B*H, Mq, M]    block scores s_ij
  *   kept_cnt  int32 [B*H, Mq]      number of kept key blocks (M for dense query blocks)
  *   kept_idx  int32 [B*H, Mq, M]   kept key-block indices, ascending, first kept_cnt valid
+ *   kept_bm   uint64 [B*H, Mq, Mpad/64] the same kept set as a bitmap (bit j%64 of word j/64)
  *   mult      uint8 [B*H, Mq, Mpad] centroid multiplicity of each key block (0 = attended exactly)
  *   cbias     fp32 [B*H, Mq, Mpad] ln(multiplicity) * sqrt(d): the centroid term's logit offset
  *             in raw q.k units, -inf where the multiplicity is 0
@@ -136,7 +138,7 @@ int solattn_check_args(int mode, const void* q, const void* k, const void* v, vo
  */
 typedef struct solattn_ws_layout {
   size_t total;
-  size_t qbar, kbar, vbar, scores, kept_cnt, kept_idx, mult, cbias, extra_cnt, extra_idx;
+  size_t qbar, kbar, vbar, scores, kept_cnt, kept_idx, kept_bm, mult, cbias, extra_cnt, extra_idx;
   size_t extra_buf, extra_part;  /* scratch of the extra-token selection                   */
   size_t kbar_bf, vbar_t, v_t;
   int Mq, M, Mpad;

@@ -48,7 +48,7 @@ def test_invalid_arguments(kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(d=96), dict(bk=32), dict(bq=32), dict(N=4000), dict(q=QP + 8),
+    dict(d=96), dict(bk=32), dict(bq=32), dict(N=4000), dict(q=QP + 8), dict(N=64 * 4097),
 ])
 def test_unsupported_shapes(kw):
     assert check(**kw) == sa.ENOTSUP
@@ -95,7 +95,7 @@ def test_page_parameter_ranges_are_accepted():
 def test_workspace_layout():
     L = sa.workspace_layout(sa.MODE_SOL, sa.BF16, 1, 24, 65536, 128, 64, 64)
     assert (L.Mq, L.M, L.Mpad) == (1024, 1024, 1024)
-    offs = [L.qbar, L.kbar, L.vbar, L.scores, L.kept_cnt, L.kept_idx, L.mult, L.cbias, L.extra_cnt,
+    offs = [L.qbar, L.kbar, L.vbar, L.scores, L.kept_cnt, L.kept_idx, L.kept_bm, L.mult, L.cbias, L.extra_cnt,
             L.extra_idx, L.extra_buf, L.extra_part, L.kbar_bf, L.vbar_t, L.v_t]
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs) and L.total > L.v_t
