@@ -46,7 +46,7 @@ class Opts(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "total", "qbar", "kbar", "vbar", "scores", "kept_cnt", "kept_idx", "kept_bm", "mult", "cbias", "extra_cnt",
-        "extra_idx", "extra_buf", "extra_part", "kbar_bf", "vbar_t", "v_t")] + [
+        "extra_idx", "extra_buf", "extra_part", "extra_flag", "kbar_bf", "vbar_t", "v_t")] + [
         ("Mq", ctypes.c_int), ("M", ctypes.c_int), ("Mpad", ctypes.c_int)]
 
 
@@ -246,6 +246,7 @@ def selection_views(workspace, mode, dtype, B, H, N, d, block_q, block_k):
         cbias=view(L.cbias, BH * Mq * Mpad, torch.float32, (BH, Mq, Mpad)),
         extra_cnt=view(L.extra_cnt, BH * Mq, torch.int32, (BH, Mq)),
         extra_idx=view(L.extra_idx, BH * Mq * MAX_EXTRA, torch.int32, (BH, Mq, MAX_EXTRA)),
+        extra_flag=view(L.extra_flag, BH * Mq, torch.int32, (BH, Mq)),
     )
 
 

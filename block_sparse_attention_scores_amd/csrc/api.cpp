@@ -140,6 +140,7 @@ int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int blo
   const int S = solattn::extra_slice_count(B, H, Mq);
   L->extra_buf = take(BH * Mq * S * 4 * solattn::EXTRA_CAP * 8);
   L->extra_part = take(BH * Mq * S * 4 * 4);
+  L->extra_flag = take(BH * Mq * 4);
   if (dtype == SOLATTN_BF16) {
     L->kbar_bf = take(BH * Mpad * d * 2);
     L->vbar_t = take(BH * Mpad * d * 2);
@@ -256,6 +257,7 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   P.extra_idx = reinterpret_cast<int*>(ws + L.extra_idx);
   P.extra_buf = reinterpret_cast<uint2*>(ws + L.extra_buf);
   P.extra_part = reinterpret_cast<int*>(ws + L.extra_part);
+  P.extra_flag = reinterpret_cast<int*>(ws + L.extra_flag);
   P.extra_slices = solattn::extra_slice_count(B, H, L.Mq);
   if (dtype == SOLATTN_BF16) {
     P.kbar_bf = reinterpret_cast<uint16_t*>(ws + L.kbar_bf);

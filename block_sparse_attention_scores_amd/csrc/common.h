@@ -41,6 +41,7 @@ struct Problem {
   int* extra_idx;
   uint2* extra_buf;      // per query block, token slice and wave: (score bits, token) candidates
   int* extra_part;       // per query block, token slice and wave: entries left after the final cut
+  int* extra_flag;       // per query block: 1 when the seeded threshold left too few candidates
   int extra_slices;      // token slices of the extra-token selection
   uint16_t* kbar_bf;
   uint16_t* vbar_t;

@@ -162,12 +162,33 @@ __device__ uint32_t wave_cut(uint2* buf, int cnt, int E, int* hist, int* scratch
   return kstar;
 }
 
+// Sample used to seed the thresholds: SAMPLE_STEPS runs of 32 consecutive tokens spread over
+// the sequence (run s: half a key block near s*M/SAMPLE_STEPS, offset by a fixed jitter).
+// Each lane keeps its SAMPLE_KEEP best candidate scores; the seed of a query block is the r-th
+// best of the kept scores, with r chosen so that about SAMPLE_MARGIN * E candidates are
+// expected at or above it (r at most the 64 kept scores).
+constexpr int SAMPLE_STEPS = 64;
+constexpr int SAMPLE_KEEP = 8;
+constexpr int SAMPLE_MARGIN = 8;
+
+__device__ __forceinline__ int sample_run(int s, int nsteps, int M) {
+  const int span = max(1, M / nsteps);
+  const int j = static_cast<int>((static_cast<long>(s) * M) / nsteps) + (s * 37) % span;
+  return j * 64 + ((nsteps > M) ? 32 * (s & 1) : 0);
+}
+
+// Pass 1.  repair = 0: every sparse query block, with thresholds seeded from the sample.
+// repair = 1: only the query blocks the merge flagged (fewer candidates than it needs), with
+// the threshold at its minimum, so that every candidate competes (the exact selection).
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P) {
-  __shared__ uint32_t thr[XR];            // shared threshold keys (0 = none yet)
+__global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P, int repair) {
+  __shared__ uint32_t thr[XR];            // shared threshold keys: append when key >= thr
   __shared__ int whist[4][256];
   __shared__ int wscr[4][4];
   __shared__ float qs[(sizeof(T) == 4) ? XR : 1][D];
+  __shared__ uint32_t samp[XR][8 * SAMPLE_KEEP];   // per query block: the best sample keys of 8 lanes
+  __shared__ int scnt[XR];                          // sample candidates per query block
+  __shared__ int any_row;
 
   const int bh = blockIdx.y, i0 = blockIdx.x * XR, slice = blockIdx.z;
   const int S = P.extra_slices;
@@ -176,8 +197,17 @@ __global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P) {
   const int rl = l % 32, i = i0 + rl;
   const int E = P.extra, N = P.N;
   const int b = bh / P.H, h = bh % P.H;
-  const bool row_ok = i < P.Mq && !(i >= P.dense_q0 && i < P.dense_q1);
   const size_t grow = (size_t)bh * P.Mq + (i < P.Mq ? i : 0);
+  bool row_ok = i < P.Mq && !(i >= P.dense_q0 && i < P.dense_q1);
+  if (repair) row_ok = row_ok && P.extra_flag[grow] != 0;
+  if (repair) {
+    // nothing to do unless one of this group's query blocks was flagged
+    if (tid == 0) any_row = 0;
+    __syncthreads();
+    if (row_ok) any_row = 1;
+    __syncthreads();
+    if (!any_row) return;
+  }
   const uint8_t* mrow = P.mult + grow * P.Mpad;
   const T* kbase = static_cast<const T*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)h * P.k.sh;
   const int ts = (((N + S - 1) / S) + 127) / 128 * 128;       // tokens per slice
@@ -208,41 +238,28 @@ __global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P) {
   }
   __syncthreads();
 
-  // candidate stores go through a buffer resource over this wave's buffers of the group's
-  // query blocks; a lane with nothing to store uses an offset past the end, which the buffer
-  // bounds check discards.  Every step issues the same number of stores, so waiting for the
-  // key prefetch never has to wait for them.
-  const uint32_t row_stride = (uint32_t)S * 4u * EXTRA_CAP * 8u;        // bytes between query blocks
-  const int nvalid = min(XR, P.Mq - i0);
-  const __amdgpu_buffer_rsrc_t brsrc =
-      xrsrc(P.extra_buf + (((size_t)bh * P.Mq + i0) * S + slice) * 4 * EXTRA_CAP + (size_t)w * EXTRA_CAP,
-            (uint32_t)(nvalid - 1) * row_stride + EXTRA_CAP * 8u);
-  const uint32_t my_off = (uint32_t)rl * row_stride;
-  // fill of this wave's buffer for the lane's query block; lanes l and l+32 share the block
-  // and keep the same count
-  int cnt = 0;
-  // bf16 path: the next step's key fragments and block flag are loaded one step ahead
+  // scores of 32 consecutive tokens from tw for this lane's query block: register r holds token
+  // tw + (r/4)*8 + (l/32)*4 + r%4
+  // (bf16: the key fragments come from kf, loaded by load_keys, which first loads the step's
+  // candidate flag into mflag, so that waiting for the flag never waits for the keys)
   bf16x8_t kf[D / 16];
-  uint8_t mnext = 0;
-  auto load_step = [&](int tw) {
-    if (tw < t_hi) {
+  uint8_t mflag = 0;
+  auto load_keys = [&](int tw) {
+    mflag = row_ok ? mrow[tw >> 6] : 0;
+    if constexpr (sizeof(T) == 2) {
       const T* kr = kbase + (int64_t)(tw + rl) * P.k.sn + 8 * (l / 32);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) kf[ks] = *reinterpret_cast<const bf16x8_t*>(kr + 16 * ks);
-      mnext = row_ok ? mrow[tw >> 6] : 0;
     }
   };
-  if constexpr (sizeof(T) == 2) load_step(t_lo + XSTEP * w);
-#pragma unroll 1
-  for (int tw = t_lo + XSTEP * w; tw < t_hi; tw += 4 * XSTEP) {
-    float acc[16];
-    bool cand;
+  // `prefetch(kc)` runs after this step's key fragments are copied out of kf (bf16), so the
+  // next step's loads can go out before this step's products
+  auto scores = [&](int tw, float* acc, auto&& prefetch) {
     if constexpr (sizeof(T) == 2) {
       bf16x8_t kc[D / 16];
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) kc[ks] = kf[ks];
-      cand = mnext > 0;
-      load_step(tw + 4 * XSTEP);
+      prefetch();
       f32x16_t c = {};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
@@ -256,19 +273,98 @@ __global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P) {
       for (int r = 0; r < 16; ++r) {
         const int tk = tw + (r / 4) * 8 + (l / 32) * 4 + (r % 4);
         const float* kr = reinterpret_cast<const float*>(kbase) + (int64_t)tk * P.k.sn;
-        float s = 0.f;
+        float sc = 0.f;
 #pragma unroll 8
-        for (int e = 0; e < D; ++e) s = fmaf(qs[rl][e], kr[e], s);
-        acc[r] = s;
+        for (int e = 0; e < D; ++e) sc = fmaf(qs[rl][e], kr[e], sc);
+        acc[r] = sc;
       }
-      cand = row_ok && mrow[tw >> 6] > 0;
+      prefetch();
     }
+  };
+
+  if (!repair) {
+    // ---- seed the thresholds.  The sample's candidates are candidates of the query block, so
+    // when at least E candidates score at or above the seed, the E best all do; the merge checks
+    // that count and sends the query block to the exact repair pass otherwise.
+    if (tid < XR) scnt[tid] = 0;
+    __syncthreads();
+    const int nsteps = min(SAMPLE_STEPS, 2 * P.M);
+    uint32_t best[SAMPLE_KEEP];             // this lane's best sample keys, descending
+#pragma unroll
+    for (int q = 0; q < SAMPLE_KEEP; ++q) best[q] = 0u;
+    int nsamp = 0;
+#pragma unroll 1
+    for (int st = w; st < nsteps; st += 4) {
+      const int tw = sample_run(st, nsteps, P.M);
+      float acc[16];
+      load_keys(tw);
+      const bool cand_s = mflag > 0;
+      scores(tw, acc, [] {});
+      if (cand_s) {
+        nsamp += 16;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          uint32_t k = float_key(acc[r]);
+#pragma unroll
+          for (int q = 0; q < SAMPLE_KEEP; ++q) {
+            const uint32_t hi = max(best[q], k), lo = min(best[q], k);
+            best[q] = hi;
+            k = lo;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < SAMPLE_KEEP; ++q) samp[rl][(w * 2 + l / 32) * SAMPLE_KEEP + q] = best[q];
+    if (nsamp) atomicAdd(&scnt[rl], nsamp);
+    __syncthreads();
+    // the r-th best kept key is the largest key with at least r kept keys >= it
+    constexpr int NK = 8 * SAMPLE_KEEP;
+    for (int task = tid; task < XR * NK; task += 256) {
+      const int rr = task / NK, a = task % NK;
+      const int ii = i0 + rr;
+      if (ii >= P.Mq || (ii >= P.dense_q0 && ii < P.dense_q1)) continue;
+      const int ncand = N - P.bk * P.kept_cnt[(size_t)bh * P.Mq + ii];
+      if (ncand <= 0) continue;
+      const long want = (static_cast<long>(SAMPLE_MARGIN) * E * scnt[rr] + ncand - 1) / ncand;
+      const int r = static_cast<int>(min(static_cast<long>(NK), max(1l, want)));
+      const uint32_t v = samp[rr][a];
+      int cge = 0;
+#pragma unroll 8
+      for (int bq = 0; bq < NK; ++bq) cge += samp[rr][bq] >= v ? 1 : 0;
+      if (cge >= r) atomicMax(&thr[rr], v);
+    }
+    __syncthreads();
+  }
+
+  // candidate stores go through a buffer resource over this wave's buffers of the group's
+  // query blocks; a lane with nothing to store uses an offset past the end, which the buffer
+  // bounds check discards.  Every step that stores issues the same number of stores.
+  const uint32_t row_stride = (uint32_t)S * 4u * EXTRA_CAP * 8u;        // bytes between query blocks
+  const int nvalid = min(XR, P.Mq - i0);
+  const __amdgpu_buffer_rsrc_t brsrc =
+      xrsrc(P.extra_buf + (((size_t)bh * P.Mq + i0) * S + slice) * 4 * EXTRA_CAP + (size_t)w * EXTRA_CAP,
+            (uint32_t)(nvalid - 1) * row_stride + EXTRA_CAP * 8u);
+  const uint32_t my_off = (uint32_t)rl * row_stride;
+  // fill of this wave's buffer for the lane's query block; lanes l and l+32 share the block
+  // and keep the same count
+  int cnt = 0;
+  // the next step's key fragments are loaded while this step is scored
+  if (t_lo + XSTEP * w < t_hi) load_keys(t_lo + XSTEP * w);
+#pragma unroll 1
+  for (int tw = t_lo + XSTEP * w; tw < t_hi; tw += 4 * XSTEP) {
+    float acc[16];
+    const bool cand = mflag > 0;
+    scores(tw, acc, [&] {
+      if (tw + 4 * XSTEP < t_hi) load_keys(tw + 4 * XSTEP);
+    });
     const uint32_t th = thr[rl];
     uint32_t bits = 0;
     if (cand) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) bits |= (float_key(acc[r]) > th ? 1u : 0u) << r;
+      for (int r = 0; r < 16; ++r) bits |= (float_key(acc[r]) >= th ? 1u : 0u) << r;
     }
+    if (__ballot(bits != 0) == 0) continue;
     // append: lane l first, then its partner l+32, each in register order
     const int mine = __popc(bits);
     const int other = __shfl_xor(mine, 32);
@@ -303,18 +399,20 @@ __global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P) {
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   // publish the buffer fills; the merge pass takes the best E over all lists of a query block
+  // (in the repair pass only for the flagged query blocks, whose lists were rebuilt)
   for (int rr = 0; rr < XR; ++rr) {
     const int ii = i0 + rr;
     if (ii >= P.Mq) break;
     const size_t row = (size_t)bh * P.Mq + ii;
     const int c = __shfl(cnt, rr);
-    if (l == 0) P.extra_part[(row * S + slice) * 4 + w] = c;
+    const bool ok = __shfl(row_ok ? 1 : 0, rr) != 0;
+    if (l == 0 && (!repair || ok)) P.extra_part[(row * S + slice) * 4 + w] = c;
   }
 }
 
 // Pass 2: best E of the 4*S partial lists of one query block, ranked by token.  The lists stay
 // in memory (L2-resident); each radix pass re-reads them.
-__global__ __launch_bounds__(64) void extra_merge_kernel(Problem P) {
+__global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) {
   __shared__ int hist[256];
   __shared__ int scr[4];
   __shared__ int toks[MAX_EXTRA];
@@ -325,12 +423,22 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P) {
   const int nl = 4 * S;
   const int* part = P.extra_part + row * nl;
   const uint2* lists = P.extra_buf + row * nl * EXTRA_CAP;
+  if (repair && P.extra_flag[row] == 0) return;
   int cnts[16];
   int total = 0;
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     cnts[q] = q < nl ? part[q] : 0;
     total += cnts[q];
+  }
+  if (!repair) {
+    // every candidate scoring at or above the seeded threshold is in the lists (or was cut in
+    // favour of better ones); fewer than min(E, |candidates|) of them means the seed was too
+    // high, and the query block goes to the exact repair pass
+    const int ncand = P.N - P.bk * P.kept_cnt[row];
+    const bool short_ = total < min(E, ncand);
+    if (l == 0) P.extra_flag[row] = short_ ? 1 : 0;
+    if (short_) return;
   }
   // visit every entry: list q, position p
   auto for_each = [&](auto&& f) {
@@ -420,18 +528,22 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P) {
 
 hipError_t launch_extra_select(const Problem& P, hipStream_t stream) {
   dim3 grid((P.Mq + XR - 1) / XR, P.B * P.H, P.extra_slices);
-  if (P.dtype == 0) {
-    if (P.d == 128) hipLaunchKernelGGL((extra_select_kernel<uint16_t, 128>), grid, dim3(256), 0, stream, P);
-    else hipLaunchKernelGGL((extra_select_kernel<uint16_t, 64>), grid, dim3(256), 0, stream, P);
-  } else {
-    if (P.d == 128) hipLaunchKernelGGL((extra_select_kernel<float, 128>), grid, dim3(256), 0, stream, P);
-    else hipLaunchKernelGGL((extra_select_kernel<float, 64>), grid, dim3(256), 0, stream, P);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   dim3 g2(P.Mq, P.B * P.H);
-  hipLaunchKernelGGL(extra_merge_kernel, g2, dim3(64), 0, stream, P);
-  return hipGetLastError();
+  for (int repair = 0; repair < 2; ++repair) {
+    if (P.dtype == 0) {
+      if (P.d == 128) hipLaunchKernelGGL((extra_select_kernel<uint16_t, 128>), grid, dim3(256), 0, stream, P, repair);
+      else hipLaunchKernelGGL((extra_select_kernel<uint16_t, 64>), grid, dim3(256), 0, stream, P, repair);
+    } else {
+      if (P.d == 128) hipLaunchKernelGGL((extra_select_kernel<float, 128>), grid, dim3(256), 0, stream, P, repair);
+      else hipLaunchKernelGGL((extra_select_kernel<float, 64>), grid, dim3(256), 0, stream, P, repair);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(extra_merge_kernel, g2, dim3(64), 0, stream, P, repair);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace solattn

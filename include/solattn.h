@@ -132,6 +132,10 @@ int solattn_check_args(int mode, const void* q, const void* k, const void* v, vo
  *   extra_idx int32 [B*H, Mq, 256] extra token indices, ascending, first extra_cnt valid
  *   extra_buf, extra_part: scratch of the extra-token selection (candidate lists per query
  *             block, token slice and wave, and their lengths)
+ *   extra_flag int32 [B*H, Mq]     1 where the extra-token selection's first pass, whose
+ *             threshold is seeded from a sample of the keys, kept fewer candidates than the
+ *             selection needs, so that the query block was selected again with every
+ *             candidate competing (the result is exact either way)
  *   kbar_bf   bf16 [B*H, Mpad, d], vbar_t bf16 [B*H, Mpad/64, d, 64], v_t bf16
  *             [B*H, M, d, 64]: operand copies for the attention kernel (bf16 only)
  * Mq = N/block_q, M = N/block_k, Mpad = M rounded up to a multiple of 64.
@@ -140,6 +144,7 @@ typedef struct solattn_ws_layout {
   size_t total;
   size_t qbar, kbar, vbar, scores, kept_cnt, kept_idx, kept_bm, mult, cbias, extra_cnt, extra_idx;
   size_t extra_buf, extra_part;  /* scratch of the extra-token selection                   */
+  size_t extra_flag;             /* int32 [B*H, Mq]: 1 = selection redone exactly            */
   size_t kbar_bf, vbar_t, v_t;
   int Mq, M, Mpad;
 } solattn_ws_layout;

@@ -96,7 +96,7 @@ def test_workspace_layout():
     L = sa.workspace_layout(sa.MODE_SOL, sa.BF16, 1, 24, 65536, 128, 64, 64)
     assert (L.Mq, L.M, L.Mpad) == (1024, 1024, 1024)
     offs = [L.qbar, L.kbar, L.vbar, L.scores, L.kept_cnt, L.kept_idx, L.kept_bm, L.mult, L.cbias, L.extra_cnt,
-            L.extra_idx, L.extra_buf, L.extra_part, L.kbar_bf, L.vbar_t, L.v_t]
+            L.extra_idx, L.extra_buf, L.extra_part, L.extra_flag, L.kbar_bf, L.vbar_t, L.v_t]
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs) and L.total > L.v_t
     assert L.scores - L.vbar >= 24 * 1024 * 128 * 4

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import block_sparse_attention_scores_amd as sa
-from gen import make_inputs, random_qkv, workload
+from gen import Inputs, Workload, bf16_round, bf16_to_f32, make_inputs, random_qkv, workload
 from oracle import dense, solattn
 from parity import Report, check_head, device_inputs, run_gpu
 
@@ -117,6 +117,29 @@ def test_few_candidates_for_extra_tokens():
     x = make_inputs(w)
     _, sel, _ = run_and_check(w, x, range(2))
     assert (sel["extra_cnt"] < 256).any()
+
+
+def test_extra_selection_exact_repair_pass():
+    # The first 32 keys of every key block score far above the rest.  At N = 4096 the extra-token
+    # selection seeds its thresholds from a sample made of exactly those keys, so the seed leaves
+    # fewer than extra_tokens candidates and every sparse query block must be selected again
+    # with every candidate competing; the result must still be the oracle's.
+    B, H, N, d = 1, 2, 4096, 128
+    rng = np.random.default_rng([11, 3])
+    u = rng.standard_normal(d).astype(np.float32)
+    u /= np.linalg.norm(u)
+    q = rng.standard_normal((B, H, N, d), dtype=np.float32) + 2.0 * u
+    k = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    k[:, :, (np.arange(N) % 64) < 32, :] += 5.0 * u
+    v = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    bits = [bf16_round(a) for a in (q, k, v)]
+    w = Workload(0, "repair", B=B, H=H, T=1, Hh=1, Ww=N, d=d, dtype="bf16", mode="sol",
+                 block_q=64, block_k=64, tau=1.3, extra_tokens=256, sink_range=128)
+    x = Inputs(w, tuple(range(H)), *[bf16_to_f32(b) for b in bits], *bits)
+    _, sel, rep = run_and_check(w, x, range(H))
+    assert rep.extra_flips == 0
+    assert (sel["extra_flag"] == 1).all(), sel["extra_flag"]
+    assert (sel["extra_cnt"] == 256).all()
 
 
 def test_batch_and_dense_rows_fp32():
