@@ -19,6 +19,8 @@
 // Pass 2 (extra_merge_kernel).  One wave per query block takes the best E of the partial lists
 // (one per wave and slice), ranks them by token, writes them out, and takes the chosen tokens
 // out of their blocks' centroid terms.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -78,26 +80,51 @@ __device__ int wave_pick_digit(const int* h, int need, int* above, int* at, int*
 
 // Radix selection over 32-bit keys held NPL per lane (valid[] marks live entries).  Finds the
 // `need`-th largest key K* and returns it; *need_eq = how many entries equal to K* are taken.
-// *cnt_eq = how many entries equal K*.
+// *cnt_eq = how many entries equal K*.  The passes start below the bits all live keys share,
+// so keys of similar magnitude take few passes and spread over many histogram bins.
 template <int NPL>
 __device__ uint32_t wave_radix_select(const uint32_t* key, const bool* valid, int need, int* hist,
                                       int* scratch, int* need_eq, int* cnt_eq) {
   const int l = threadIdx.x & 63;
-  uint32_t prefix = 0, pmask = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  int n = 0;
+#pragma unroll
+  for (int u = 0; u < NPL; ++u)
+    if (valid[u]) {
+      kmin = min(kmin, key[u]);
+      kmax = max(kmax, key[u]);
+      ++n;
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
+    kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+    n += __shfl_xor(n, o);
+  }
+  const uint32_t diff = kmin ^ kmax;
+  if (diff == 0u) {                         // all live keys equal
+    *need_eq = need;
+    *cnt_eq = n;
+    return kmax;
+  }
+  const int hb = 31 - __builtin_clz(diff);
+  uint32_t pmask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = kmax & pmask;
   int at = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  for (int top = hb; top >= 0; top -= 8) {
+    const int shift = top >= 7 ? top - 7 : 0;
+    const uint32_t dmask = (2u << (top - shift)) - 1u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) hist[4 * l + q] = 0;
     wave_sync();
 #pragma unroll
     for (int u = 0; u < NPL; ++u)
-      if (valid[u] && (key[u] & pmask) == prefix) atomicAdd(&hist[(key[u] >> shift) & 255u], 1);
+      if (valid[u] && (key[u] & pmask) == prefix) atomicAdd(&hist[(key[u] >> shift) & dmask], 1);
     wave_sync();
     int above;
     const int dg = wave_pick_digit(hist, need, &above, &at, scratch);
     prefix |= static_cast<uint32_t>(dg) << shift;
-    pmask |= 0xFFu << shift;
+    pmask |= dmask << shift;
     need -= above;
   }
   *need_eq = need;
@@ -169,7 +196,7 @@ __device__ uint32_t wave_cut(uint2* buf, int cnt, int E, int* hist, int* scratch
 // expected at or above it (r at most the 64 kept scores).
 constexpr int SAMPLE_STEPS = 64;
 constexpr int SAMPLE_KEEP = 8;
-constexpr int SAMPLE_MARGIN = 8;
+constexpr int SAMPLE_MARGIN = 6;
 
 __device__ __forceinline__ int sample_run(int s, int nsteps, int M) {
   const int span = max(1, M / nsteps);
@@ -411,7 +438,53 @@ __global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P, int rep
 }
 
 // Pass 2: best E of the 4*S partial lists of one query block, ranked by token.  The lists stay
-// in memory (L2-resident); each radix pass re-reads them.
+// in memory (L2-resident) and every pass reads them as one flat range with 8 loads in flight
+// per lane.  Radix selection starts below the bits that all keys share (scores of one query
+// block have similar magnitudes), so it takes few passes and its histogram counts spread over
+// many bins.
+
+// `need`-th largest of the keys visited by `visit(f)` (f(key) for every live key), radix 8 over
+// the bits below the common prefix of [kmin, kmax].  Returns it; *need_eq = how many of the keys
+// equal to it are taken, *cnt_eq = how many keys equal it.
+template <typename Visit>
+__device__ uint32_t merge_select(Visit&& visit, uint32_t kmin, uint32_t kmax, int need, int* hist,
+                                 int* scr, int* need_eq, int* cnt_eq) {
+  const int l = threadIdx.x & 63;
+  const uint32_t diff = kmin ^ kmax;
+  if (diff == 0u) {                       // every key equal
+    int n = 0;
+    visit([&](uint32_t) { ++n; });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+    *need_eq = need;
+    *cnt_eq = n;
+    return kmax;
+  }
+  const int hb = 31 - __builtin_clz(diff);
+  uint32_t pmask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = kmax & pmask;
+  int at = 0;
+  for (int top = hb; top >= 0; top -= 8) {
+    const int shift = top >= 7 ? top - 7 : 0;
+    const uint32_t dmask = (2u << (top - shift)) - 1u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hist[4 * l + q] = 0;
+    wave_sync();
+    visit([&](uint32_t k) {
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1);
+    });
+    wave_sync();
+    int above;
+    const int dg = wave_pick_digit(hist, need, &above, &at, scr);
+    prefix |= static_cast<uint32_t>(dg) << shift;
+    pmask |= dmask << shift;
+    need -= above;
+  }
+  *need_eq = need;
+  *cnt_eq = at;
+  return prefix;
+}
+
 __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) {
   __shared__ int hist[256];
   __shared__ int scr[4];
@@ -440,85 +513,136 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) 
     if (l == 0) P.extra_flag[row] = short_ ? 1 : 0;
     if (short_) return;
   }
-  // visit every entry: list q, position p
-  auto for_each = [&](auto&& f) {
-#pragma unroll 1
-    for (int q = 0; q < nl; ++q) {
-      const uint2* lq = lists + q * EXTRA_CAP;
-      for (int p = l; p < cnts[q]; p += 64) f(lq[p]);
-    }
+  // the lists as one flat range: entry p lives in list q with start[q] <= p < start[q+1]
+  int start[17];
+  start[0] = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) start[q + 1] = start[q] + cnts[q];
+  auto entry = [&](int p) {
+    int q = 0;
+#pragma unroll
+    for (int r = 1; r < 16; ++r) q += p >= start[r] ? 1 : 0;
+    return lists[q * EXTRA_CAP + (p - start[q])];
   };
-  uint32_t kstar = 0, tmax = 0xFFFFFFFFu;
-  bool all = total <= E;
-  if (!all) {
-    // radix select of the E-th best key
-    uint32_t prefix = 0, pmask = 0;
-    int need = E, at = 0;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hist[4 * l + q] = 0;
-      wave_sync();
-      for_each([&](uint2 e) {
-        const uint32_t k = float_key(__uint_as_float(e.x));
-        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
-      });
-      wave_sync();
-      int above;
-      const int dg = wave_pick_digit(hist, need, &above, &at, scr);
-      prefix |= static_cast<uint32_t>(dg) << shift;
-      pmask |= 0xFFu << shift;
-      need -= above;
-    }
-    kstar = prefix;
-    if (need < at) {
-      // ties at K*: keep the `need` lowest tokens -> radix select on inverted tokens
-      uint32_t p2 = 0, m2 = 0;
-      int need2 = need, at2 = 0;
-      for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) hist[4 * l + q] = 0;
-        wave_sync();
-        for_each([&](uint2 e) {
-          const uint32_t k = float_key(__uint_as_float(e.x));
-          const uint32_t k2 = ~e.y;
-          if (k == kstar && (k2 & m2) == p2) atomicAdd(&hist[(k2 >> shift) & 255u], 1);
-        });
-        wave_sync();
-        int above;
-        const int dg = wave_pick_digit(hist, need2, &above, &at2, scr);
-        p2 |= static_cast<uint32_t>(dg) << shift;
-        m2 |= 0xFFu << shift;
-        need2 -= above;
-      }
-      tmax = ~p2;
-    }
-  }
-  // survivors -> LDS (any order), then rank by token
   if (l == 0) scr[3] = 0;
   wave_sync();
-  for_each([&](uint2 e) {
-    const uint32_t k = float_key(__uint_as_float(e.x));
-    if (all || k > kstar || (k == kstar && e.y <= tmax)) toks[atomicAdd(&scr[3], 1)] = static_cast<int>(e.y);
-  });
+  // The usual case: every entry in registers (NPL per lane), selected there, survivors
+  // appended to toks[].  Larger lists take the streaming path below.
+  auto in_registers = [&](auto nplc) {
+    constexpr int NPL = decltype(nplc)::value;
+    uint32_t key[NPL], tok[NPL];
+    bool valid[NPL], keep[NPL];
+#pragma unroll
+    for (int u = 0; u < NPL; ++u) {
+      const int p = u * 64 + l;
+      valid[u] = p < total;
+      const uint2 e = valid[u] ? entry(p) : make_uint2(0u, 0u);
+      key[u] = float_key(__uint_as_float(e.x));
+      tok[u] = e.y;
+    }
+    wave_best<NPL>(key, tok, valid, total, E, hist, scr, keep);
+#pragma unroll
+    for (int u = 0; u < NPL; ++u) {
+      const uint64_t m = __ballot(keep[u]);
+      if (keep[u]) toks[scr[3] + __popcll(m & ((1ull << l) - 1ull))] = static_cast<int>(tok[u]);
+      wave_sync();
+      if (l == 0) scr[3] += __popcll(m);
+      wave_sync();
+    }
+  };
+  if (total <= 16 * 64) {
+    in_registers(std::integral_constant<int, 16>{});
+  } else if (total <= 32 * 64) {
+    in_registers(std::integral_constant<int, 32>{});
+  } else {
+    // streaming: every pass reads the lists again, 8 loads in flight per lane
+    auto for_each = [&](auto&& f) {
+#pragma unroll 1
+      for (int p0 = 0; p0 < total; p0 += 8 * 64) {
+        uint2 e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int p = p0 + u * 64 + l;
+          e[u] = p < total ? entry(p) : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (p0 + u * 64 + l < total) f(float_key(__uint_as_float(e[u].x)), e[u].y);
+      }
+    };
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    for_each([&](uint32_t k, uint32_t) {
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
+    });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
+      kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+    }
+    int need_eq, cnt_eq;
+    const uint32_t kstar = merge_select([&](auto&& f) { for_each([&](uint32_t k, uint32_t) { f(k); }); },
+                                        kmin, kmax, E, hist, scr, &need_eq, &cnt_eq);
+    uint32_t tmax = 0xFFFFFFFFu;
+    if (need_eq < cnt_eq) {
+      // ties at K*: keep the need_eq lowest tokens (larger ~token = smaller token)
+      uint32_t tmin2 = 0xFFFFFFFFu, tmax2 = 0u;
+      for_each([&](uint32_t k, uint32_t t) {
+        if (k == kstar) {
+          tmin2 = min(tmin2, ~t);
+          tmax2 = max(tmax2, ~t);
+        }
+      });
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        tmin2 = min(tmin2, static_cast<uint32_t>(__shfl_xor(static_cast<int>(tmin2), o)));
+        tmax2 = max(tmax2, static_cast<uint32_t>(__shfl_xor(static_cast<int>(tmax2), o)));
+      }
+      int ne2, ce2;
+      tmax = ~merge_select([&](auto&& f) {
+        for_each([&](uint32_t k, uint32_t t) {
+          if (k == kstar) f(~t);
+        });
+      }, tmin2, tmax2, need_eq, hist, scr, &ne2, &ce2);
+    }
+    for_each([&](uint32_t k, uint32_t t) {
+      if (k > kstar || (k == kstar && t <= tmax)) toks[atomicAdd(&scr[3], 1)] = static_cast<int>(t);
+    });
+  }
   wave_sync();
+  // survivors are in toks[0..c) in any order: sort them ascending (bitonic network over
+  // MAX_EXTRA slots, padding at the end), write them out, and take them out of their key
+  // blocks' centroid terms (key blocks are 64 tokens: block_k is 64 in this library)
   const int c = scr[3];
+  for (int p = c + l; p < MAX_EXTRA; p += 64) toks[p] = 0x7fffffff;
+  wave_sync();
+#pragma unroll 1
+  for (int kk = 2; kk <= MAX_EXTRA; kk <<= 1) {
+#pragma unroll 1
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+#pragma unroll
+      for (int p = l; p < MAX_EXTRA; p += 64) {
+        const int pj = p ^ j;
+        if (pj > p) {
+          const int x = toks[p], y = toks[pj];
+          if ((x > y) == ((p & kk) == 0)) {
+            toks[p] = y;
+            toks[pj] = x;
+          }
+        }
+      }
+      wave_sync();
+    }
+  }
   int* out = P.extra_idx + row * MAX_EXTRA;
   uint8_t* mr = P.mult + row * P.Mpad;
   for (int p = l; p < c; p += 64) {
-    const int t = toks[p], bt = t / P.bk;
-    int rank = 0, same = 0, same_before = 0;
-    for (int q = 0; q < c; ++q) {
-      const int o = toks[q];
-      rank += o < t;
-      const bool sb = (o / P.bk) == bt;
-      same += sb;
-      same_before += sb && o < t;
-    }
-    out[rank] = t;
-    if (same_before == 0) {
-      const int m = P.bk - same;
+    const int t = toks[p], bt = t >> 6;
+    out[p] = t;
+    if (p == 0 || (toks[p - 1] >> 6) != bt) {
+      int e = p + 1;
+      while (e < c && (toks[e] >> 6) == bt) ++e;
+      const int m = 64 - (e - p);
       mr[bt] = static_cast<uint8_t>(m);
       P.cbias[row * P.Mpad + bt] = m > 0 ? __logf(static_cast<float>(m)) / P.scale : -__builtin_inff();
     }
