@@ -29,6 +29,39 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+CSRC = os.path.join(ROOT, "block_sparse_attention_scores_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_flash_fwd_traffic_sol-full-bf16-n64k.md")
+
+
+def sources_digest():
+    """sha256 (first 16 hex digits) of the library's kernel sources, in name order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per sparse_flash_fwd launch from the committed counter summary, or None when
+    the summary is for another workload or the kernel sources changed since it was taken."""
+    if workload_name != "sol-full-bf16-n64k" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.strip().startswith(("sources_sha256", "traffic_bytes_per_launch")):
+            k, v = line.strip().strip("`").split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("sources_sha256") != sources_digest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,10 +227,15 @@ def main():
     t_flash = kern["sparse_flash_fwd"]["avg_ms"] * 1e-3
     ach = f_exact / t_flash / 1e12
     roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None,
+                frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic(w.name),
                 kernel="sparse_flash_fwd", algorithmic_flop=f_exact)
     # the other kernels against their own rooflines
+    # pool: read Q, K, V; write the fp32 means, and for bf16 the transposed V tiles and the
+    # bf16 copies of the pooled keys and values
+    Mpad = (M + 63) // 64 * 64
     pool_bytes = BH * (3 * w.N * w.d * es + (Mq + 2 * M) * w.d * 4)
+    if w.dtype == "bf16":
+        pool_bytes += BH * (w.N * w.d * 2 + 2 * Mpad * w.d * 2)
     if "block_pool" in kern:
         t = kern["block_pool"]["avg_ms"] * 1e-3
         kern["block_pool"].update(bound="hbm", achieved_GBs=round(pool_bytes / t / 1e9, 1),

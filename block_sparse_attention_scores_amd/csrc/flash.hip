@@ -107,7 +107,7 @@ struct TileIter {
 // heaviest) come first, then the rest head-major.  Consecutive units go to the same XCD in runs
 // of XCD_RUN (workgroups are dealt to the 8 XCDs round-robin), so one XCD works on neighbouring
 // query blocks of one head and shares their key tiles in its L2.
-constexpr int XCD_RUN = 64;
+constexpr int XCD_RUN = 16;
 
 __device__ __forceinline__ bool flash_unit(const Problem& P, int G, int gid, int* bh, int* pair) {
   const int x = gid % 8, k = gid / 8;
@@ -348,13 +348,6 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
       for (int dt = 0; dt < D / 32; ++dt)
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], pcur, o[dt], 0, 0, 0);
       if (ks + 1 < 4) {
-        // one product, then a slice of the next step's vector work, four times
-        __builtin_amdgcn_sched_group_barrier(0x100, D / 32, 0);    // LDS reads of step ks+1
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x406, 7, 0);      // VALU incl. exp
-        }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) va[dt] = vn[dt];
         pcur = pnext;
