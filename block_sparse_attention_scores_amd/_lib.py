@@ -27,6 +27,9 @@ class SolattnError(RuntimeError):
         super().__init__(f"libsolattn status {status} ({status_string(status)}): {detail}")
 
 
+FLAG_EXACT_EXTRA = 1   # SOLATTN_FLAG_EXACT_EXTRA
+
+
 class Opts(ctypes.Structure):
     _fields_ = [
         ("struct_size", ctypes.c_int),
@@ -40,6 +43,7 @@ class Opts(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("flags", ctypes.c_uint),
     ]
 
 
@@ -112,7 +116,7 @@ def workspace_bytes(mode, dtype, B, H, N, d, block_q, block_k) -> int:
 
 
 def make_opts(dtype=BF16, strides=None, dense_rows=(0, 0), workspace=0, workspace_bytes=0,
-              stream=0) -> Opts:
+              stream=0, flags=0) -> Opts:
     o = Opts()
     o.struct_size = ctypes.sizeof(Opts)
     o.dtype = dtype
@@ -125,6 +129,7 @@ def make_opts(dtype=BF16, strides=None, dense_rows=(0, 0), workspace=0, workspac
     o.workspace = workspace or None
     o.workspace_bytes = int(workspace_bytes)
     o.stream = stream or None
+    o.flags = int(flags)
     return o
 
 
@@ -177,7 +182,7 @@ def alloc_workspace(mode, q, block_q, block_k):
 
 
 def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, extra_tokens,
-          dense_rows, out, workspace, stream):
+          dense_rows, out, workspace, stream, flags=0):
     torch = _torch()
     B, H, N, d = q.shape
     for n, t in (("k", k), ("v", v)):
@@ -192,7 +197,7 @@ def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, ext
         stream = torch.cuda.current_stream(q.device).cuda_stream
     strides = [tuple(t.stride()[:3]) for t in (q, k, v, out)]
     opts = make_opts(_dtype_code(q), strides, dense_rows, workspace.data_ptr(),
-                     workspace.numel() * workspace.element_size(), stream)
+                     workspace.numel() * workspace.element_size(), stream, flags)
     L = lib()
     if mode == MODE_SOL:
         rc = L.sol_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
@@ -207,20 +212,22 @@ def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, ext
 
 
 def sol_attn(q, k, v, *, tau=1.3, block_q=64, block_k=64, sink_range=0, extra_tokens=0,
-             dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False):
+             dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False,
+             flags=0):
     """sol-attn forward on [B, H, N, d] GPU tensors (bfloat16 or float32); see include/solattn.h."""
     o, ws = _call(MODE_SOL, q, k, v, tau=tau, keep_percent=0.0, block_q=block_q, block_k=block_k,
                   sink_range=sink_range, extra_tokens=extra_tokens, dense_rows=dense_rows, out=out,
-                  workspace=workspace, stream=stream)
+                  workspace=workspace, stream=stream, flags=flags)
     return (o, ws) if return_workspace else o
 
 
 def sla_attn(q, k, v, *, keep_percent=10.0, block_q=128, block_k=64, sink_range=0, extra_tokens=0,
-             dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False):
+             dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False,
+             flags=0):
     """sla forward on [B, H, N, d] GPU tensors (bfloat16 or float32); see include/solattn.h."""
     o, ws = _call(MODE_SLA, q, k, v, tau=0.0, keep_percent=keep_percent, block_q=block_q,
                   block_k=block_k, sink_range=sink_range, extra_tokens=extra_tokens,
-                  dense_rows=dense_rows, out=out, workspace=workspace, stream=stream)
+                  dense_rows=dense_rows, out=out, workspace=workspace, stream=stream, flags=flags)
     return (o, ws) if return_workspace else o
 
 

@@ -235,6 +235,7 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   }
   P.sink_blocks = (sink_range + block_k - 1) / block_k;
   P.extra = extra_tokens;
+  P.exact_extra = (opts && (opts->flags & SOLATTN_FLAG_EXACT_EXTRA)) ? 1 : 0;
   const int d0 = opts ? opts->dense_row_begin : 0, d1 = opts ? opts->dense_row_end : 0;
   P.dense_q0 = d0 / block_q;
   P.dense_q1 = d1 / block_q;

@@ -24,6 +24,7 @@ struct Problem {
   int k_sla;             // sla: ceil(keep_percent * M / 100)
   int sink_blocks;       // key blocks overlapping [0, sink_range)
   int extra;             // extra tokens per query block (0..256)
+  int exact_extra;       // select extra tokens exactly from the start (no seeded pass)
   int dense_q0, dense_q1;  // query blocks [dense_q0, dense_q1) attend every key
   float scale;           // 1/sqrt(d)
   Tensor q, k, v, o;

@@ -485,6 +485,8 @@ __device__ uint32_t merge_select(Visit&& visit, uint32_t kmin, uint32_t kmax, in
   return prefix;
 }
 
+// repair: 0 = first merge (checks the seeded pass), 1 = merge of the repaired query blocks,
+// 2 = flag every sparse query block for the exact pass (no merge)
 __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) {
   __shared__ int hist[256];
   __shared__ int scr[4];
@@ -496,6 +498,10 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) 
   const int nl = 4 * S;
   const int* part = P.extra_part + row * nl;
   const uint2* lists = P.extra_buf + row * nl * EXTRA_CAP;
+  if (repair == 2) {                                       // exact selection for every row
+    if (l == 0) P.extra_flag[row] = 1;
+    return;
+  }
   if (repair && P.extra_flag[row] == 0) return;
   int cnts[16];
   int total = 0;
@@ -653,7 +659,7 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) 
 hipError_t launch_extra_select(const Problem& P, hipStream_t stream) {
   dim3 grid((P.Mq + XR - 1) / XR, P.B * P.H, P.extra_slices);
   dim3 g2(P.Mq, P.B * P.H);
-  for (int repair = 0; repair < 2; ++repair) {
+  auto pass1 = [&](int repair) {
     if (P.dtype == 0) {
       if (P.d == 128) hipLaunchKernelGGL((extra_select_kernel<uint16_t, 128>), grid, dim3(256), 0, stream, P, repair);
       else hipLaunchKernelGGL((extra_select_kernel<uint16_t, 64>), grid, dim3(256), 0, stream, P, repair);
@@ -661,13 +667,21 @@ hipError_t launch_extra_select(const Problem& P, hipStream_t stream) {
       if (P.d == 128) hipLaunchKernelGGL((extra_select_kernel<float, 128>), grid, dim3(256), 0, stream, P, repair);
       else hipLaunchKernelGGL((extra_select_kernel<float, 64>), grid, dim3(256), 0, stream, P, repair);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(extra_merge_kernel, g2, dim3(64), 0, stream, P, repair);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+  };
+  hipError_t e;
+  if (P.exact_extra) {
+    // every query block straight to the exact pass
+    hipLaunchKernelGGL(extra_merge_kernel, g2, dim3(64), 0, stream, P, 2);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    if ((e = pass1(0)) != hipSuccess) return e;
+    hipLaunchKernelGGL(extra_merge_kernel, g2, dim3(64), 0, stream, P, 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  return hipSuccess;
+  if ((e = pass1(1)) != hipSuccess) return e;
+  hipLaunchKernelGGL(extra_merge_kernel, g2, dim3(64), 0, stream, P, 1);
+  return hipGetLastError();
 }
 
 }  // namespace solattn

@@ -71,7 +71,17 @@ typedef struct solattn_opts {
   void*  workspace;               /* device buffer owned by the caller, or NULL            */
   size_t workspace_bytes;         /* its size; must be >= solattn_workspace_bytes(...)     */
   void*  stream;                  /* hipStream_t; NULL = null stream                       */
+  unsigned flags;                 /* SOLATTN_FLAG_* bits; 0 = defaults                       */
 } solattn_opts;
+
+/*
+ * SOLATTN_FLAG_EXACT_EXTRA: the extra-token selection skips its sampled first pass (which
+ * seeds each query block's running threshold from a sample of the keys and falls back to the
+ * exact pass for the query blocks it leaves short) and runs the exact pass for every query
+ * block.  The selected tokens are the same either way; the flag only costs time.  It exists
+ * to exercise and check the exact pass on any input.
+ */
+#define SOLATTN_FLAG_EXACT_EXTRA 1u
 
 /*
  * sol-attn forward.

@@ -32,15 +32,15 @@ def device_inputs(x):
 
 
 def run_gpu(mode, q, k, v, *, block_q, block_k, tau=1.3, keep_percent=10.0, sink_range=0,
-            extra_tokens=0, dense_rows=(0, 0)):
+            extra_tokens=0, dense_rows=(0, 0), flags=0):
     if mode == "sol":
         out, ws = sa.sol_attn(q, k, v, tau=tau, block_q=block_q, block_k=block_k,
                               sink_range=sink_range, extra_tokens=extra_tokens,
-                              dense_rows=dense_rows, return_workspace=True)
+                              dense_rows=dense_rows, return_workspace=True, flags=flags)
     else:
         out, ws = sa.sla_attn(q, k, v, keep_percent=keep_percent, block_q=block_q,
                               block_k=block_k, sink_range=sink_range, extra_tokens=extra_tokens,
-                              dense_rows=dense_rows, return_workspace=True)
+                              dense_rows=dense_rows, return_workspace=True, flags=flags)
     torch.cuda.synchronize()
     B, H, N, d = q.shape
     dt = sa.BF16 if q.dtype == torch.bfloat16 else sa.FP32

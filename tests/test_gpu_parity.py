@@ -25,17 +25,17 @@ def params(w, **ov):
     return p
 
 
-def run_and_check(w, x, heads_to_check, qblocks=None, mode=None, **ov):
+def run_and_check(w, x, heads_to_check, qblocks=None, mode=None, flags=0, **ov):
     mode = mode or w.mode
     p = params(w, **ov)
-    print(f"\n[parity] {w.name} mode={mode} H={x.q.shape[1]} N={w.N} {p}", flush=True)
+    print(f"\n[parity] {w.name} mode={mode} H={x.q.shape[1]} N={w.N} flags={flags} {p}", flush=True)
     q, k, v = device_inputs(x)
-    out, sel = run_gpu(mode, q, k, v, **p)
+    out, sel = run_gpu(mode, q, k, v, flags=flags, **p)
     rep = Report()
     for h in heads_to_check:
         xin = (x.q[0, h].astype(np.float64), x.k[0, h].astype(np.float64), x.v[0, h].astype(np.float64))
         ref = solattn.head_forward(mode, *xin, **p, want_out=False)
-        qb = qblocks(h, ref) if callable(qblocks) else qblocks
+        qb = qblocks(h, ref, sel) if callable(qblocks) else qblocks
         check_head(mode, ref, sel, h, x_in=xin, d=w.d, N=w.N, report=rep, qblocks=qb,
                    out_gpu=out[0, h], dtype=x.w.dtype, **p)
     print(f"[parity] rows={rep.rows} mask_flips={rep.mask_flips} extra_flips={rep.extra_flips} "
@@ -69,15 +69,21 @@ def test_sol_bf16_extra_partial_tiles(extra):
     run_and_check(w, x, range(1))
 
 
-def _sample(rng_seed, n_sparse=6, n_dense=2):
-    def pick(h, ref):
+def _sample(rng_seed, n_sparse=6, n_dense=2, n_flagged=2):
+    # random sparse and dense query blocks, plus query blocks whose extra tokens were selected
+    # by the exact pass after the sampled pass fell short (if any)
+    def pick(h, ref, sel):
         rng = np.random.default_rng(rng_seed + h)
         sparse = np.flatnonzero(~ref["dense"])
         dn = np.flatnonzero(ref["dense"])
         out = list(rng.choice(sparse, size=min(n_sparse, sparse.size), replace=False))
         if dn.size:
             out += list(rng.choice(dn, size=min(n_dense, dn.size), replace=False))
-        return sorted(int(i) for i in out)
+        fl = np.flatnonzero(sel["extra_flag"][h] == 1)
+        fl = fl[~ref["dense"][fl]]
+        if fl.size:
+            out += list(rng.choice(fl, size=min(n_flagged, fl.size), replace=False))
+        return sorted(set(int(i) for i in out))
     return pick
 
 
@@ -119,11 +125,11 @@ def test_few_candidates_for_extra_tokens():
     assert (sel["extra_cnt"] < 256).any()
 
 
-def test_extra_selection_exact_repair_pass():
-    # The first 32 keys of every key block score far above the rest.  At N = 4096 the extra-token
-    # selection seeds its thresholds from a sample made of exactly those keys, so the seed leaves
-    # fewer than extra_tokens candidates and every sparse query block must be selected again
-    # with every candidate competing; the result must still be the oracle's.
+@pytest.mark.parametrize("flags", [0, sa.FLAG_EXACT_EXTRA])
+def test_extra_selection_exact_pass(flags):
+    # The first 32 keys of every key block score far above the rest, a distribution far from the
+    # sampled pass's assumptions; with SOLATTN_FLAG_EXACT_EXTRA every query block takes the exact
+    # pass (flagged in extra_flag).  Either way the selection must be the oracle's.
     B, H, N, d = 1, 2, 4096, 128
     rng = np.random.default_rng([11, 3])
     u = rng.standard_normal(d).astype(np.float32)
@@ -136,9 +142,10 @@ def test_extra_selection_exact_repair_pass():
     w = Workload(0, "repair", B=B, H=H, T=1, Hh=1, Ww=N, d=d, dtype="bf16", mode="sol",
                  block_q=64, block_k=64, tau=1.3, extra_tokens=256, sink_range=128)
     x = Inputs(w, tuple(range(H)), *[bf16_to_f32(b) for b in bits], *bits)
-    _, sel, rep = run_and_check(w, x, range(H))
+    _, sel, rep = run_and_check(w, x, range(H), flags=flags)
     assert rep.extra_flips == 0
-    assert (sel["extra_flag"] == 1).all(), sel["extra_flag"]
+    if flags:
+        assert (sel["extra_flag"] == 1).all(), sel["extra_flag"]
     assert (sel["extra_cnt"] == 256).all()
 
 
