@@ -262,7 +262,7 @@ def main():
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         t0 = time.perf_counter()
-        cpu = cpu_baseline(w, x)
+        cpu = cpu_baseline(w, x, heads=tuple(range(min(4, w.H))), n_sparse=96, n_dense=24)
         log(f"[bench] oracle sample took {time.perf_counter() - t0:.1f} s")
 
     res = {

@@ -189,8 +189,9 @@ __device__ uint32_t wave_cut(uint2* buf, int cnt, int E, int* hist, int* scratch
   return kstar;
 }
 
-// Sample used to seed the thresholds: SAMPLE_STEPS runs of 32 consecutive tokens spread over
-// the sequence (run s: half a key block near s*M/SAMPLE_STEPS, offset by a fixed jitter).
+// Sample used to seed the thresholds: runs of 32 consecutive tokens spread over the sequence
+// (run s of n: half a key block near s*M/n, offset by a fixed jitter), SAMPLE_STEPS of them or
+// one per 1024 tokens, whichever is more (at most 4 * SAMPLE_STEPS).
 // Each lane keeps its SAMPLE_KEEP best candidate scores; the seed of a query block is the r-th
 // best of the kept scores, with r chosen so that about SAMPLE_MARGIN * E candidates are
 // expected at or above it (r at most the 64 kept scores).
@@ -315,7 +316,9 @@ __global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P, int rep
     // that count and sends the query block to the exact repair pass otherwise.
     if (tid < XR) scnt[tid] = 0;
     __syncthreads();
-    const int nsteps = min(SAMPLE_STEPS, 2 * P.M);
+    // the sample grows with the sequence (one run per 1024 tokens, 64 to 256 runs), so that its
+    // share of a long sequence's candidates, and with it the rank used below, stays large
+    const int nsteps = min(2 * P.M, min(4 * SAMPLE_STEPS, max(SAMPLE_STEPS, N / 1024)));
     uint32_t best[SAMPLE_KEEP];             // this lane's best sample keys, descending
 #pragma unroll
     for (int q = 0; q < SAMPLE_KEEP; ++q) best[q] = 0u;
