@@ -34,13 +34,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_flash_fwd_traffic_sol-full
 
 
 def sources_digest():
-    """sha256 (first 16 hex digits) of the library's kernel sources, in name order."""
+    """sha256 (first 16 hex digits) of the attention kernel's sources (the kernel file and the
+    headers it includes), in name order: the traffic counters belong to that kernel."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
+    for f in ("common.h", "flash.hip", "launch.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -53,7 +53,7 @@ def measured_traffic(workload_name):
     for line in open(TRAFFIC_FILE):
         if ":" in line and line.strip().startswith(("sources_sha256", "traffic_bytes_per_launch")):
             k, v = line.strip().strip("`").split(":", 1)
-            fields[k.strip()] = v.strip().strip("`")
+            fields[k.split()[0]] = v.strip().strip("`")
     if fields.get("sources_sha256") != sources_digest():
         return None
     try:
