@@ -1,4 +1,5 @@
-"""Plain fp64 CPU oracle of the block-sparse attention forward (sol-attn and sla).
+"""Plain fp64 CPU oracle of the block-sparse attention forward (sol-attn, sla and the static
+local 3-D neighbourhood pattern).
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
 module; only the tests, the smoke check and the bench's CPU-baseline leg do.  It
@@ -9,6 +10,10 @@ Sources (pages on the ComfyUI "BlockSparseAttention" node and its relatives):
              tables "通用输入" (common inputs), "sol-attn 输入", "sla 输入".
   [node-ja]  the same document in Japanese (tables "共通入力", "sol-attn 入力", "sla 入力").
   [star7]    README of the minimax-h3-chunk-star7 node pack, sections "SLA" and "Sol".
+  [h3-bsa]   the article on why block sparse attention matters for H3 in ComfyUI, section 1:
+             a fixed pattern keeping the centre block, its neighbours one frame back and
+             forward, and its spatial neighbours one block up, down, left and right; every
+             other block is zero.
 
 The method, step by step (one (batch, head) problem at a time; every problem is
 independent):
@@ -35,6 +40,16 @@ independent):
               kept blocks plus centroid terms merged in one FP32 online softmax).
   Query rows inside the dense row range attend every key exactly
   ([node-zh] common-inputs table, sink_conditioning row: exact_kv_and_rows).
+  local3d replaces step 3 by the fixed pattern of [h3-bsa] section 1 (no scores are
+  used) and drops skipped blocks in step 5 like sla.  The sequence is a video grid of
+  frames x height x width tokens in raster order (frame-major, then row, then column)
+  and blocks are runs of consecutive tokens, so the pattern is stated on tokens and
+  lifted to blocks: key block j is kept for query block i when some token of j is a
+  token of i or one of its six grid neighbours (same row and column one frame away,
+  same frame and column one row away, same frame and row one column away).  When a
+  frame holds a whole number of blocks and a block holds a whole number of rows, or
+  a row a whole number of blocks, this is exactly the centre / +-1 frame / +-1 block
+  up, down, left, right stencil on the grid of blocks.
 
 Readings where the pages are silent (each listed in the design notes):
   c = 1/sqrt(d); non-causal; mean pooling over the block's actual tokens; strict
@@ -132,6 +147,33 @@ def select_sla(s_row: np.ndarray, keep_percent: float, forced: np.ndarray) -> np
     return keep
 
 
+def local3d_neighbours(i: int, N: int, block_q: int, block_k: int, grid) -> np.ndarray:
+    """Key blocks holding a token of query block i or a grid neighbour of one ([h3-bsa] §1).
+
+    grid = (frames, height, width) with frames*height*width == N; token p sits at frame
+    p // (height*width), row (p % (height*width)) // width, column p % width.  Neighbours
+    differ by one in exactly one coordinate and stay inside the grid (no wrap-around).
+    """
+    F, Hh, Ww = (int(g) for g in grid)
+    assert F * Hh * Ww == N, "the grid must cover the sequence"
+    M = -(-N // block_k)
+    keep = np.zeros(M, dtype=bool)
+    p = np.arange(i * block_q, min((i + 1) * block_q, N))
+    t, rem = np.divmod(p, Hh * Ww)
+    y, x = np.divmod(rem, Ww)
+    for dt, dy, dx in ((0, 0, 0), (-1, 0, 0), (1, 0, 0), (0, -1, 0), (0, 1, 0), (0, 0, -1),
+                       (0, 0, 1)):
+        tt, yy, xx = t + dt, y + dy, x + dx
+        ok = (tt >= 0) & (tt < F) & (yy >= 0) & (yy < Hh) & (xx >= 0) & (xx < Ww)
+        keep[(tt[ok] * Hh * Ww + yy[ok] * Ww + xx[ok]) // block_k] = True
+    return keep
+
+
+def select_local3d(neighbours: np.ndarray, forced: np.ndarray) -> np.ndarray:
+    """Static local routing ([h3-bsa] §1): the neighbourhood plus the forced blocks."""
+    return forced | neighbours
+
+
 # ---------------------------------------------------------------- step 4
 
 def extra_select(e_row: np.ndarray, kept: np.ndarray, block_k: int, n_extra: int) -> np.ndarray:
@@ -191,8 +233,10 @@ def attend_rows(qr: np.ndarray, k: np.ndarray, v: np.ndarray, kbar: np.ndarray,
 def head_forward(mode: str, q: np.ndarray, k: np.ndarray, v: np.ndarray, *, block_q: int,
                  block_k: int, tau: float = 1.3, keep_percent: float = 10.0, sink_range: int = 0,
                  extra_tokens: int = 0, dense_rows=(0, 0), selection=None, qblocks=None,
-                 want_out: bool = True):
+                 want_out: bool = True, grid=None):
     """The pass for one (batch, head): q, k, v [N, d] (any float dtype, widened to fp64).
+
+    mode: "sol", "sla" or "local3d" (which needs grid = (frames, height, width)).
 
     Returns a dict with
       out     [N, d] fp64 (rows of query blocks not in `qblocks` are NaN),
@@ -204,7 +248,8 @@ def head_forward(mode: str, q: np.ndarray, k: np.ndarray, v: np.ndarray, *, bloc
       qbar, kbar, vbar.
     `selection=(kept, extra)` replaces steps 3-4 with the given lists.
     """
-    assert mode in ("sol", "sla")
+    assert mode in ("sol", "sla", "local3d")
+    assert mode != "local3d" or grid is not None, "local3d needs the video grid"
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -236,8 +281,10 @@ def head_forward(mode: str, q: np.ndarray, k: np.ndarray, v: np.ndarray, *, bloc
                 if tau != -math.inf:
                     mu, sd = row_stats(s[i])
                     theta[i] = mu + tau * sd if sd > 0 else mu
-            else:
+            elif mode == "sla":
                 kept[i] = select_sla(s[i], keep_percent, f)
+            else:
+                kept[i] = select_local3d(local3d_neighbours(i, N, block_q, block_k, grid), f)
         if extra_tokens > 0:
             for i0 in range(0, Mq, 64):
                 rows = [i for i in range(i0, min(i0 + 64, Mq)) if not dense[i]]
