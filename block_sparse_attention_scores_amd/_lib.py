@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "solattn.h")
 
 OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 BF16, FP32 = 0, 1
-MODE_SOL, MODE_SLA = 0, 1
+MODE_SOL, MODE_SLA, MODE_LOCAL3D = 0, 1, 2
 MAX_EXTRA = 256
 NKERNELS = 5
 
@@ -70,8 +70,12 @@ def lib() -> ctypes.CDLL:
     L.sol_attn_fwd.restype = i
     L.sla_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, ctypes.POINTER(Opts)]
     L.sla_attn_fwd.restype = i
+    L.local3d_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(Opts)]
+    L.local3d_attn_fwd.restype = i
     L.solattn_check_args.argtypes = [i, vp, vp, vp, vp, i, i, i, i, f, f, i, i, i, i, ctypes.POINTER(Opts)]
     L.solattn_check_args.restype = i
+    L.local3d_check_args.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(Opts)]
+    L.local3d_check_args.restype = i
     L.solattn_workspace_layout.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(WsLayout)]
     L.solattn_workspace_layout.restype = i
     L.solattn_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
@@ -182,7 +186,7 @@ def alloc_workspace(mode, q, block_q, block_k):
 
 
 def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, extra_tokens,
-          dense_rows, out, workspace, stream, flags=0):
+          dense_rows, out, workspace, stream, flags=0, grid=None):
     torch = _torch()
     B, H, N, d = q.shape
     for n, t in (("k", k), ("v", v)):
@@ -202,6 +206,11 @@ def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, ext
     if mode == MODE_SOL:
         rc = L.sol_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
                             float(tau), block_q, block_k, sink_range, extra_tokens, ctypes.byref(opts))
+    elif mode == MODE_LOCAL3D:
+        F, Hh, Ww = (int(g) for g in grid)
+        rc = L.local3d_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
+                                F, Hh, Ww, block_q, block_k, sink_range, extra_tokens,
+                                ctypes.byref(opts))
     else:
         rc = L.sla_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
                             block_q, block_k, sink_range, extra_tokens, float(keep_percent),
@@ -228,6 +237,20 @@ def sla_attn(q, k, v, *, keep_percent=10.0, block_q=128, block_k=64, sink_range=
     o, ws = _call(MODE_SLA, q, k, v, tau=0.0, keep_percent=keep_percent, block_q=block_q,
                   block_k=block_k, sink_range=sink_range, extra_tokens=extra_tokens,
                   dense_rows=dense_rows, out=out, workspace=workspace, stream=stream, flags=flags)
+    return (o, ws) if return_workspace else o
+
+
+def local3d_attn(q, k, v, *, grid, block_q=64, block_k=64, sink_range=0, extra_tokens=0,
+                 dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False,
+                 flags=0):
+    """Static local 3-D neighbourhood forward on [B, H, N, d] GPU tensors; grid = (frames,
+    height, width) with frames*height*width == N; see include/solattn.h."""
+    if len(grid) != 3:
+        raise ValueError("grid must be (frames, height, width)")
+    o, ws = _call(MODE_LOCAL3D, q, k, v, tau=0.0, keep_percent=100.0, block_q=block_q,
+                  block_k=block_k, sink_range=sink_range, extra_tokens=extra_tokens,
+                  dense_rows=dense_rows, out=out, workspace=workspace, stream=stream, flags=flags,
+                  grid=grid)
     return (o, ws) if return_workspace else o
 
 

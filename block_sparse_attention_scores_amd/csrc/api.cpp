@@ -1,6 +1,7 @@
 // libsolattn C ABI: argument validation, workspace planning and the launch sequence
 //   block_pool -> block_score -> block_select -> extra_select -> sparse_flash_fwd
-// on the caller's stream (see include/solattn.h for the contract).
+// on the caller's stream (see include/solattn.h for the contract).  The local 3-D mode
+// needs no block scores and skips block_score.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -52,10 +53,12 @@ void extent(const void* p, Strides s, int B, int H, int N, int d, size_t es, uin
   *hi = base + static_cast<uintptr_t>(last + 1) * es;
 }
 
+// grid: {frames, height, width} for SOLATTN_MODE_LOCAL3D, ignored otherwise.
 int check(int mode, const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
           float tau, float keep_percent, int block_q, int block_k, int sink_range, int extra_tokens,
-          const solattn_opts* opts, Strides st[4]) {
-  if (mode != SOLATTN_MODE_SOL && mode != SOLATTN_MODE_SLA) return fail(SOLATTN_EINVAL, "mode %d", mode);
+          const solattn_opts* opts, Strides st[4], const int* grid) {
+  if (mode != SOLATTN_MODE_SOL && mode != SOLATTN_MODE_SLA && mode != SOLATTN_MODE_LOCAL3D)
+    return fail(SOLATTN_EINVAL, "mode %d", mode);
   if (opts && opts->struct_size != (int)sizeof(solattn_opts))
     return fail(SOLATTN_EINVAL, "opts->struct_size %d != %d", opts->struct_size, (int)sizeof(solattn_opts));
   const int dtype = opts ? opts->dtype : SOLATTN_BF16;
@@ -66,6 +69,12 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   if (mode == SOLATTN_MODE_SOL && std::isnan(tau)) return fail(SOLATTN_EINVAL, "tau is NaN");
   if (mode == SOLATTN_MODE_SLA && !(keep_percent > 0.f && keep_percent <= 100.f))
     return fail(SOLATTN_EINVAL, "keep_percent %g outside (0, 100]", (double)keep_percent);
+  if (mode == SOLATTN_MODE_LOCAL3D) {
+    if (grid[0] < 1 || grid[1] < 1 || grid[2] < 1)
+      return fail(SOLATTN_EINVAL, "grid %d x %d x %d", grid[0], grid[1], grid[2]);
+    if ((int64_t)grid[0] * grid[1] * grid[2] != N)
+      return fail(SOLATTN_EINVAL, "grid %d x %d x %d does not hold N=%d tokens", grid[0], grid[1], grid[2], N);
+  }
   if (extra_tokens < 0 || extra_tokens > SOLATTN_MAX_EXTRA)
     return fail(SOLATTN_EINVAL, "extra_tokens %d outside [0, %d]", extra_tokens, SOLATTN_MAX_EXTRA);
   if (sink_range < 0 || sink_range > N) return fail(SOLATTN_EINVAL, "sink_range %d outside [0, N]", sink_range);
@@ -100,6 +109,8 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   if ((int64_t)B * H > 65535) return fail(SOLATTN_ENOTSUP, "B*H=%lld too large", (long long)B * H);
   if (dtype == SOLATTN_BF16 && N / block_k > solattn::MAX_BLOCKS_BF16)
     return fail(SOLATTN_ENOTSUP, "bf16: more than %d key blocks", solattn::MAX_BLOCKS_BF16);
+  if (mode == SOLATTN_MODE_LOCAL3D && N / block_k > solattn::MAX_BLOCKS_LOCAL3D)
+    return fail(SOLATTN_ENOTSUP, "local 3-D: more than %d key blocks", solattn::MAX_BLOCKS_LOCAL3D);
   for (int t = 0; t < 4; ++t)   // the kernels address up to 64 rows with 32-bit byte offsets
     if (st[t].sn >= (int64_t(1) << 24)) return fail(SOLATTN_ENOTSUP, "row stride of %c too large", "qkvo"[t]);
   for (int t = 0; t < 4; ++t) {
@@ -184,11 +195,13 @@ hipEvent_t take_event() {
 
 int run(int mode, const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
         float tau, float keep_percent, int block_q, int block_k, int sink_range, int extra_tokens,
-        const solattn_opts* opts) {
+        const solattn_opts* opts, const int* grid = nullptr) {
   g_err.clear();
   Strides st[4];
+  const int no_grid[3] = {0, 0, 0};
+  if (!grid) grid = no_grid;
   int rc = check(mode, q, k, v, out, B, H, N, d, tau, keep_percent, block_q, block_k, sink_range,
-                 extra_tokens, opts, st);
+                 extra_tokens, opts, st, grid);
   if (rc != SOLATTN_OK) return rc;
   const int dtype = opts ? opts->dtype : SOLATTN_BF16;
   solattn_ws_layout L;
@@ -208,10 +221,13 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
     std::lock_guard<std::mutex> lk(g_ws_mu);
     if (g_ws_size[dev] < L.total) {
       if (g_ws[dev]) {
-        hipDeviceSynchronize();
-        hipFree(g_ws[dev]);
+        // earlier calls on any stream may still read the old buffer
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return fail(SOLATTN_EHIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+        e = hipFree(g_ws[dev]);
         g_ws[dev] = nullptr;
         g_ws_size[dev] = 0;
+        if (e != hipSuccess) return fail(SOLATTN_EHIP, "hipFree: %s", hipGetErrorString(e));
       }
       void* p = nullptr;
       if (hipMalloc(&p, L.total) != hipSuccess) return fail(SOLATTN_EHIP, "hipMalloc(%zu) failed", L.total);
@@ -240,6 +256,7 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   P.dense_q0 = d0 / block_q;
   P.dense_q1 = d1 / block_q;
   if (P.dense_q1 <= P.dense_q0) P.dense_q0 = P.dense_q1 = 0;
+  P.frames = grid[0]; P.height = grid[1]; P.width = grid[2];
   P.scale = 1.0f / std::sqrt(static_cast<float>(d));
   P.q = Tensor{q, st[0].sb, st[0].sh, st[0].sn};
   P.k = Tensor{k, st[1].sb, st[1].sh, st[1].sn};
@@ -270,44 +287,63 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   const bool timing = g_timing;
   TimedCall tc;
   std::memset(&tc, 0, sizeof tc);
+  auto release = [&]() {
+    for (int e = 0; e <= NK; ++e)
+      if (tc.ev[e]) g_free_events.push_back(tc.ev[e]);
+  };
   if (timing) {
     for (int e = 0; e <= NK; ++e) {
       tc.ev[e] = take_event();
-      if (!tc.ev[e]) return fail(SOLATTN_EHIP, "hipEventCreate");
+      if (!tc.ev[e]) {
+        release();
+        return fail(SOLATTN_EHIP, "hipEventCreate");
+      }
     }
   } else {
     tl.unlock();
   }
+  bool mark_ok = true;
   auto mark = [&](int e) {
-    if (timing) hipEventRecord(tc.ev[e], stream);
+    if (timing && hipEventRecord(tc.ev[e], stream) != hipSuccess) mark_ok = false;
   };
 
+  // The launch sequence; returns the failing kernel's name, or nullptr.
   const bool do_extra = extra_tokens > 0 && !P.keep_all;
-  hipError_t err;
-  mark(0);
-  if ((err = solattn::launch_block_pool(P, stream)) != hipSuccess)
-    return fail(SOLATTN_EHIP, "block_pool: %s", hipGetErrorString(err));
-  tc.ran[0] = true;
-  mark(1);
-  if ((err = solattn::launch_block_score(P, stream)) != hipSuccess)
-    return fail(SOLATTN_EHIP, "block_score: %s", hipGetErrorString(err));
-  tc.ran[1] = true;
-  mark(2);
-  if ((err = solattn::launch_block_select(P, stream)) != hipSuccess)
-    return fail(SOLATTN_EHIP, "block_select: %s", hipGetErrorString(err));
-  tc.ran[2] = true;
-  mark(3);
-  if (do_extra) {
-    if ((err = solattn::launch_extra_select(P, stream)) != hipSuccess)
-      return fail(SOLATTN_EHIP, "extra_select: %s", hipGetErrorString(err));
-    tc.ran[3] = true;
+  hipError_t err = hipSuccess;
+  auto launch_all = [&]() -> const char* {
+    mark(0);
+    if ((err = solattn::launch_block_pool(P, stream)) != hipSuccess) return "block_pool";
+    tc.ran[0] = true;
+    mark(1);
+    if (mode != SOLATTN_MODE_LOCAL3D) {
+      if ((err = solattn::launch_block_score(P, stream)) != hipSuccess) return "block_score";
+      tc.ran[1] = true;
+    }
+    mark(2);
+    if ((err = solattn::launch_block_select(P, stream)) != hipSuccess) return "block_select";
+    tc.ran[2] = true;
+    mark(3);
+    if (do_extra) {
+      if ((err = solattn::launch_extra_select(P, stream)) != hipSuccess) return "extra_select";
+      tc.ran[3] = true;
+    }
+    mark(4);
+    if ((err = solattn::launch_sparse_flash(P, stream)) != hipSuccess) return "sparse_flash_fwd";
+    tc.ran[4] = true;
+    mark(5);
+    return nullptr;
+  };
+  if (const char* failed = launch_all()) {
+    if (timing) release();
+    return fail(SOLATTN_EHIP, "%s: %s", failed, hipGetErrorString(err));
   }
-  mark(4);
-  if ((err = solattn::launch_sparse_flash(P, stream)) != hipSuccess)
-    return fail(SOLATTN_EHIP, "sparse_flash_fwd: %s", hipGetErrorString(err));
-  tc.ran[4] = true;
-  mark(5);
-  if (timing) g_calls.push_back(tc);
+  if (timing) {
+    if (!mark_ok) {
+      release();
+      return fail(SOLATTN_EHIP, "hipEventRecord failed (the kernels were enqueued)");
+    }
+    g_calls.push_back(tc);
+  }
   return SOLATTN_OK;
 }
 
@@ -327,13 +363,34 @@ int sla_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, 
              extra_tokens, opts);
 }
 
+int local3d_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                     int frames, int height, int width, int block_q, int block_k, int sink_range,
+                     int extra_tokens, const solattn_opts* opts) {
+  const int grid[3] = {frames, height, width};
+  return run(SOLATTN_MODE_LOCAL3D, q, k, v, out, B, H, N, d, 0.f, 100.f, block_q, block_k, sink_range,
+             extra_tokens, opts, grid);
+}
+
 int solattn_check_args(int mode, const void* q, const void* k, const void* v, void* out, int B, int H, int N,
                        int d, float tau, float keep_percent, int block_q, int block_k, int sink_range,
                        int extra_tokens, const solattn_opts* opts) {
   g_err.clear();
   Strides st[4];
+  if (mode == SOLATTN_MODE_LOCAL3D)
+    return fail(SOLATTN_EINVAL, "mode %d: use local3d_check_args", mode);
+  const int no_grid[3] = {0, 0, 0};
   return check(mode, q, k, v, out, B, H, N, d, tau, keep_percent, block_q, block_k, sink_range, extra_tokens,
-               opts, st);
+               opts, st, no_grid);
+}
+
+int local3d_check_args(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                       int frames, int height, int width, int block_q, int block_k, int sink_range,
+                       int extra_tokens, const solattn_opts* opts) {
+  g_err.clear();
+  Strides st[4];
+  const int grid[3] = {frames, height, width};
+  return check(SOLATTN_MODE_LOCAL3D, q, k, v, out, B, H, N, d, 0.f, 100.f, block_q, block_k, sink_range,
+               extra_tokens, opts, st, grid);
 }
 
 int solattn_workspace_layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k,

@@ -17,7 +17,7 @@ struct Problem {
   int B, H, N, d;
   int bq, bk;            // query / key block sizes
   int Mq, M, Mpad;       // query blocks, key blocks, key blocks rounded up to 64
-  int mode;              // 0 sol, 1 sla
+  int mode;              // 0 sol, 1 sla, 2 static local 3-D neighbourhood
   int dtype;             // 0 bf16, 1 fp32
   float tau;
   int keep_all;          // tau == -inf: every block kept
@@ -26,6 +26,7 @@ struct Problem {
   int extra;             // extra tokens per query block (0..256)
   int exact_extra;       // select extra tokens exactly from the start (no seeded pass)
   int dense_q0, dense_q1;  // query blocks [dense_q0, dense_q1) attend every key
+  int frames, height, width;  // local 3-D mode: the token grid (frames*height*width == N)
   float scale;           // 1/sqrt(d)
   Tensor q, k, v, o;
   // workspace
@@ -50,6 +51,8 @@ struct Problem {
 };
 
 constexpr int MAX_EXTRA = 256;
+// The local 3-D mode marks a query block's neighbourhood in a bitmap of M bits in LDS.
+constexpr int MAX_BLOCKS_LOCAL3D = 65536;
 // The bf16 attention kernel holds a query block's kept-block bitmap in one 64-bit word per lane.
 constexpr int MAX_BLOCKS_BF16 = 64 * 64;
 // Candidate buffer per (query block, token slice, wave) of the extra-token selection.  It is cut

@@ -4,7 +4,12 @@
 //     std the population deviation over all M blocks (two passes).
 //   sla (node docs, sla table, keep_percent row): keep the k highest non-forced blocks,
 //     ties to the lower index (radix select on order-preserving keys).
-//   Sink blocks and the diagonal block(s) are kept on top in both modes (node docs, sla
+//   local 3-D (the article on block sparse attention for H3 in ComfyUI, section 1): a fixed
+//     pattern with no scores.  The sequence is a frames x height x width token grid in raster
+//     order; key block j is kept when it holds a token of the query block or a grid neighbour
+//     of one (one step along one axis, no wrap-around).  Where the grid of blocks exists this
+//     is the centre, +-1 frame and +-1 block up/down/left/right stencil.
+//   Sink blocks and the diagonal block(s) are kept on top in every mode (node docs, sla
 //   table, and sink_conditioning row).  Query blocks in the dense row range keep every block.
 // The kept set is written twice: as an ascending index list and as a bitmap (bit j of word
 // j/64), which the attention kernel walks without touching memory.
@@ -49,6 +54,7 @@ __device__ int block_scan_incl(int v, int* sh, int* total) {
 }
 
 __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
+  extern __shared__ uint32_t nbm[];   // local 3-D mode: neighbourhood bitmap, Mpad/32 words
   __shared__ float fsh[4];
   __shared__ int ish[4];
   __shared__ int hist[256];
@@ -106,6 +112,28 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
     const float var = block_sum(acc2, fsh) / static_cast<float>(M);
     const float sd = sqrtf(var);
     theta = sd > 0.f ? fmaf(P.tau, sd, mu) : mu;
+  } else if (P.mode == 2) {
+    // one thread per query token: mark the blocks of the token and of its grid neighbours
+    for (int wd = tid; wd < P.Mpad / 32; wd += 256) nbm[wd] = 0u;
+    __syncthreads();
+    if (tid < P.bq) {
+      const int hw = P.height * P.width;
+      const int p = i * P.bq + tid;
+      const int t = p / hw, r = p - t * hw;
+      const int y = r / P.width, x = r - y * P.width;
+      auto mark = [&](int tok) {
+        const int j = tok / P.bk;
+        atomicOr(&nbm[j >> 5], 1u << (j & 31));
+      };
+      mark(p);
+      if (t > 0) mark(p - hw);
+      if (t + 1 < P.frames) mark(p + hw);
+      if (y > 0) mark(p - P.width);
+      if (y + 1 < P.height) mark(p + P.width);
+      if (x > 0) mark(p - 1);
+      if (x + 1 < P.width) mark(p + 1);
+    }
+    __syncthreads();
   } else {
     const int nforced = min(P.sink_blocks, M) + (diag_hi - diag_lo + 1) -
                         max(0, min(diag_hi, P.sink_blocks - 1) - diag_lo + 1);
@@ -153,6 +181,8 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
         keep = true;
       } else if (P.mode == 0) {
         keep = s[j] > theta;
+      } else if (P.mode == 2) {
+        keep = (nbm[j >> 5] >> (j & 31)) & 1u;
       } else if (sla_any) {
         const uint32_t key = float_key(s[j]);
         keep = key > kstar;
@@ -187,7 +217,8 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
 
 hipError_t launch_block_select(const Problem& P, hipStream_t stream) {
   dim3 grid(P.Mq, P.B * P.H);
-  hipLaunchKernelGGL(block_select_kernel, grid, dim3(256), 0, stream, P);
+  const size_t lds = P.mode == 2 ? (size_t)(P.Mpad / 32) * 4 : 0;
+  hipLaunchKernelGGL(block_select_kernel, grid, dim3(256), lds, stream, P);
   return hipGetLastError();
 }
 

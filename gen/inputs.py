@@ -44,7 +44,7 @@ class Workload:
     Ww: int
     d: int
     dtype: str                 # "bf16" or "fp32"
-    mode: str                  # "sol" or "sla"
+    mode: str                  # "sol", "sla" or "local3d"
     block_q: int
     block_k: int
     tau: float = 1.3

@@ -1,5 +1,6 @@
 /*
- * libsolattn: block-sparse attention forward (sol-attn and sla) for AMD gfx950.
+ * libsolattn: block-sparse attention forward (sol-attn, sla and a static local
+ * 3-D neighbourhood pattern) for AMD gfx950.
  *
  * The operation (ComfyUI "BlockSparseAttention" node docs, input tables; the
  * minimax-h3-chunk-star7 README, sections "Sol" and "SLA"), per (batch, head):
@@ -50,6 +51,7 @@ extern "C" {
 /* Selection modes. */
 #define SOLATTN_MODE_SOL 0
 #define SOLATTN_MODE_SLA 1
+#define SOLATTN_MODE_LOCAL3D 2
 
 /* Largest extra_tokens value (node docs, extra_tokens row: 0..256). */
 #define SOLATTN_MAX_EXTRA 256
@@ -115,12 +117,45 @@ int sla_attn_fwd(const void* q, const void* k, const void* v, void* out,
                  const solattn_opts* opts);
 
 /*
- * Host-only argument check: the exact validation the two calls above perform,
- * without launching anything.  mode is SOLATTN_MODE_SOL or SOLATTN_MODE_SLA
- * (keep_percent is ignored for sol, tau for sla).  Returns a status code.
+ * Static local 3-D neighbourhood forward (the article on block sparse attention
+ * for H3 in ComfyUI, section 1: a fixed pattern that keeps the centre block, its
+ * neighbours one frame back and forward and its spatial neighbours one block up,
+ * down, left and right, and zeroes every other block).  Step 3 above is replaced
+ * by that pattern (no block scores are computed; the workspace's scores are not
+ * written) and skipped blocks contribute nothing, as in sla.
+ *   frames, height, width  the token grid, >= 1 each, frames*height*width == N
+ *             (else SOLATTN_EINVAL).  Token p sits at frame p / (height*width),
+ *             row (p % (height*width)) / width, column p % width.
+ *   Key block j is kept for query block i when it holds a token of i or a grid
+ *   neighbour of one (one step along one axis, no wrap-around).  When a frame is
+ *   a whole number of key blocks and a row is a whole number of blocks (or a
+ *   block a whole number of rows) this is exactly the centre / +-1 frame / +-1
+ *   block row / +-1 block column stencil on the grid of blocks; for other grids
+ *   it is the same rule at token level.  Sink blocks, the diagonal, the dense
+ *   row range and extra_tokens work as in sol_attn_fwd.
+ *   At most 65536 key blocks (SOLATTN_ENOTSUP beyond); the other arguments and
+ *   limits are those of sol_attn_fwd.
+ */
+int local3d_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                     int B, int H, int N, int d, int frames, int height, int width,
+                     int block_q, int block_k, int sink_range, int extra_tokens,
+                     const solattn_opts* opts);
+
+/*
+ * Host-only argument check: the exact validation sol_attn_fwd / sla_attn_fwd
+ * perform, without launching anything.  mode is SOLATTN_MODE_SOL or
+ * SOLATTN_MODE_SLA (keep_percent is ignored for sol, tau for sla);
+ * SOLATTN_MODE_LOCAL3D returns SOLATTN_EINVAL (use local3d_check_args).
+ * Returns a status code.
  */
 int solattn_check_args(int mode, const void* q, const void* k, const void* v, void* out,
                        int B, int H, int N, int d, float tau, float keep_percent,
+                       int block_q, int block_k, int sink_range, int extra_tokens,
+                       const solattn_opts* opts);
+
+/* Host-only argument check of local3d_attn_fwd.  Returns a status code. */
+int local3d_check_args(const void* q, const void* k, const void* v, void* out,
+                       int B, int H, int N, int d, int frames, int height, int width,
                        int block_q, int block_k, int sink_range, int extra_tokens,
                        const solattn_opts* opts);
 
@@ -131,7 +166,7 @@ int solattn_check_args(int mode, const void* q, const void* k, const void* v, vo
  *   qbar      fp32 [B*H, Mq, d]    pooled queries
  *   kbar      fp32 [B*H, M, d]     pooled keys
  *   vbar      fp32 [B*H, M, d]     pooled values
- *   scores    fp32 [B*H, Mq, M]    block scores s_ij
+ *   scores    fp32 [B*H, Mq, M]    block scores s_ij (not written by local3d_attn_fwd)
  *   kept_cnt  int32 [B*H, Mq]      number of kept key blocks (M for dense query blocks)
  *   kept_idx  int32 [B*H, Mq, M]   kept key-block indices, ascending, first kept_cnt valid
  *   kept_bm   uint64 [B*H, Mq, Mpad/64] the same kept set as a bitmap (bit j%64 of word j/64)
@@ -175,7 +210,8 @@ const char* solattn_last_error(void);
 
 /*
  * Per-kernel timing.  While enabled, every call records HIP events around each
- * of its kernel launches on the call's stream.  solattn_timing_read waits for
+ * of its kernel launches on the call's stream (local3d_attn_fwd launches no
+ * block_score).  solattn_timing_read waits for
  * those events, writes the summed milliseconds and launch counts per kernel
  * (index order: block_pool, block_score, block_select, extra_select,
  * sparse_flash_fwd) into ms[0..n) and launches[0..n), and resets the sums.

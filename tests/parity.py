@@ -5,7 +5,8 @@ Tolerances:
   * pooled means: fp32 sums of 64 values, |Δ| <= 4e-6 * max|input| of the head;
   * block scores: one fp32 dot product of d terms, |Δ| <= 1e-5 * scale * (|q̄| . |k̄|);
   * kept masks: bit-exact except blocks whose fp64 score lies within 1e-4 * σ_i of the row's
-    threshold (sol) or of the k-th non-forced score (sla); such flips are counted;
+    threshold (sol) or of the k-th non-forced score (sla); such flips are counted.  The static
+    local 3-D pattern uses no scores: its masks are bit-exact, and its scores are not written;
   * extra sets (rows whose masks agree): exact except tokens within 1e-4 * σ_e of the boundary
     score, σ_e the std of the row's candidate scores;
   * outputs, against the oracle run on the GPU's own selection: bf16 max-abs 2e-2 and
@@ -31,9 +32,16 @@ def device_inputs(x):
     return tuple(torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (x.q, x.k, x.v))
 
 
+MODES = {"sol": sa.MODE_SOL, "sla": sa.MODE_SLA, "local3d": sa.MODE_LOCAL3D}
+
+
 def run_gpu(mode, q, k, v, *, block_q, block_k, tau=1.3, keep_percent=10.0, sink_range=0,
-            extra_tokens=0, dense_rows=(0, 0), flags=0):
-    if mode == "sol":
+            extra_tokens=0, dense_rows=(0, 0), flags=0, grid=None):
+    if mode == "local3d":
+        out, ws = sa.local3d_attn(q, k, v, grid=grid, block_q=block_q, block_k=block_k,
+                                  sink_range=sink_range, extra_tokens=extra_tokens,
+                                  dense_rows=dense_rows, return_workspace=True, flags=flags)
+    elif mode == "sol":
         out, ws = sa.sol_attn(q, k, v, tau=tau, block_q=block_q, block_k=block_k,
                               sink_range=sink_range, extra_tokens=extra_tokens,
                               dense_rows=dense_rows, return_workspace=True, flags=flags)
@@ -44,8 +52,7 @@ def run_gpu(mode, q, k, v, *, block_q, block_k, tau=1.3, keep_percent=10.0, sink
     torch.cuda.synchronize()
     B, H, N, d = q.shape
     dt = sa.BF16 if q.dtype == torch.bfloat16 else sa.FP32
-    views = sa.selection_views(ws, sa.MODE_SOL if mode == "sol" else sa.MODE_SLA, dt, B, H, N, d,
-                               block_q, block_k)
+    views = sa.selection_views(ws, MODES[mode], dt, B, H, N, d, block_q, block_k)
     sel = {k_: v_.cpu().numpy() for k_, v_ in views.items()}
     return out.float().cpu().numpy().astype(np.float64), sel
 
@@ -76,7 +83,7 @@ class Report:
 
 def check_head(mode, ref, sel, bh, *, x_in, d, block_k, tau, keep_percent, sink_range, block_q,
                N, extra_tokens, report, qblocks=None, out_gpu=None, q=None, k=None, v=None,
-               dense_rows=(0, 0), dtype="bf16"):
+               dense_rows=(0, 0), dtype="bf16", grid=None):
     """Compare one head's intermediates and (sampled) outputs. ref = oracle head_forward dict."""
     Mq, M = ref["kept"].shape
     scale = 1.0 / math.sqrt(d)
@@ -85,10 +92,11 @@ def check_head(mode, ref, sel, bh, *, x_in, d, block_k, tau, keep_percent, sink_
     for name in ("qbar", "kbar", "vbar"):
         g = sel[name][bh].astype(np.float64)
         np.testing.assert_allclose(g, ref[name], rtol=0, atol=4e-6 * mx, err_msg=name)
-    # scores
-    bound = 1e-5 * scale * (np.abs(ref["qbar"]) @ np.abs(ref["kbar"]).T) + 1e-30
-    ds = np.abs(sel["scores"][bh].astype(np.float64) - ref["scores"])
-    assert (ds <= bound).all(), f"score error {ds.max()} > bound"
+    # scores (the static local pattern computes none)
+    if mode != "local3d":
+        bound = 1e-5 * scale * (np.abs(ref["qbar"]) @ np.abs(ref["kbar"]).T) + 1e-30
+        ds = np.abs(sel["scores"][bh].astype(np.float64) - ref["scores"])
+        assert (ds <= bound).all(), f"score error {ds.max()} > bound"
     # masks
     gmask = gpu_kept_mask(sel, bh, M)
     s = ref["scores"]
@@ -99,6 +107,7 @@ def check_head(mode, ref, sel, bh, *, x_in, d, block_k, tau, keep_percent, sink_
         diff = np.flatnonzero(gmask[i] != ref["kept"][i])
         if diff.size == 0:
             continue
+        assert mode != "local3d", f"row {i}: static pattern differs at blocks {diff}"
         mu, sd = solattn.row_stats(s[i])
         if mode == "sol":
             edge = mu + tau * sd if sd > 0 else mu
@@ -150,7 +159,7 @@ def check_head(mode, ref, sel, bh, *, x_in, d, block_k, tau, keep_percent, sink_
         inj = solattn.head_forward(mode, x_in[0], x_in[1], x_in[2], block_q=block_q, block_k=block_k,
                                    tau=tau, keep_percent=keep_percent, sink_range=sink_range,
                                    extra_tokens=extra_tokens, dense_rows=dense_rows,
-                                   selection=(gmask, gextra), qblocks=qblocks)
+                                   selection=(gmask, gextra), qblocks=qblocks, grid=grid)
         rows = np.flatnonzero(~np.isnan(inj["out"][:, 0]))
         err = np.abs(out_gpu[rows] - inj["out"][rows])
         report.max_abs = max(report.max_abs, float(err.max()))

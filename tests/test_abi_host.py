@@ -80,6 +80,39 @@ def test_forward_calls_fail_before_launching():
     assert rc == sa.EINVAL and "keep_percent" in sa.last_error()
 
 
+def check3(grid=(4, 16, 64), N=4096, fp32=False, **kw):
+    a = dict(q=QP, k=KP, v=VP, o=OP, B=1, H=2, d=64, bq=64, bk=64, sink=0, extra=0)
+    a.update(kw)
+    o = sa.make_opts(dtype=sa.FP32) if fp32 else None
+    return sa.lib().local3d_check_args(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], N, a["d"],
+                                       *grid, a["bq"], a["bk"], a["sink"], a["extra"],
+                                       ctypes.byref(o) if o is not None else None)
+
+
+def test_local3d_validation():
+    assert check3() == sa.OK
+    assert check3(grid=(1, 1, 4096)) == sa.OK
+    assert check3(grid=(3, 5, 448), N=105 * 64) == sa.OK          # any grid that holds N tokens
+    assert check3(grid=(4, 45, 80), N=14400) == sa.OK             # frames that straddle blocks
+    assert check3(bq=128, extra=256, sink=512) == sa.OK
+    for g in [(0, 64, 64), (4, -1, 64), (4, 16, 0), (4, 16, 65), (2, 16, 64)]:
+        assert check3(grid=g) == sa.EINVAL, g
+        assert "grid" in sa.last_error()
+    assert check3(grid=(1 << 16, 1 << 16, 1 << 16)) == sa.EINVAL   # product overflows int32
+    assert check3(extra=257) == sa.EINVAL
+    assert check3(bk=32) == sa.ENOTSUP
+    # the neighbourhood bitmap bounds the key blocks (bf16 is bounded earlier)
+    N = 64 * 65537
+    assert check3(grid=(65537, 1, 64), N=N, fp32=True) == sa.ENOTSUP
+    assert "local 3-D" in sa.last_error()
+    assert check3(grid=(65536, 1, 64), N=N - 64, fp32=True) == sa.OK
+    # the sol/sla check refuses the mode that needs a grid
+    assert check(mode=sa.MODE_LOCAL3D) == sa.EINVAL
+    L = sa.lib()
+    rc = L.local3d_attn_fwd(QP, KP, VP, OP, 1, 2, 4096, 64, 4, 16, 63, 64, 64, 0, 0, None)
+    assert rc == sa.EINVAL and "grid" in sa.last_error()
+
+
 def test_page_parameter_ranges_are_accepted():
     g = json.load(open(GOLDEN))
     assert check(extra=g["extra_tokens_range"]["max"]) == sa.OK

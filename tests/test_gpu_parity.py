@@ -18,16 +18,18 @@ from parity import Report, check_head, device_inputs, run_gpu
 pytestmark = pytest.mark.gpu
 
 
-def params(w, **ov):
+def params(w, mode=None, **ov):
     p = dict(block_q=w.block_q, block_k=w.block_k, tau=w.tau, keep_percent=w.keep_percent,
              sink_range=w.sink_range, extra_tokens=w.extra_tokens, dense_rows=w.dense_rows)
+    if (mode or w.mode) == "local3d":
+        p["grid"] = (w.T, w.Hh, w.Ww)
     p.update(ov)
     return p
 
 
 def run_and_check(w, x, heads_to_check, qblocks=None, mode=None, flags=0, **ov):
     mode = mode or w.mode
-    p = params(w, **ov)
+    p = params(w, mode, **ov)
     print(f"\n[parity] {w.name} mode={mode} H={x.q.shape[1]} N={w.N} flags={flags} {p}", flush=True)
     q, k, v = device_inputs(x)
     out, sel = run_gpu(mode, q, k, v, flags=flags, **p)
@@ -97,6 +99,36 @@ def test_sol_long_n203k_all_heads():
     w = workload(5)
     x = make_inputs(w)
     run_and_check(w, x, [5], qblocks=_sample(50, n_sparse=4))
+
+
+@pytest.mark.parametrize("extra", [0, 64])
+def test_local3d_fp32_tiny(extra):
+    # 32-token rows: a block holds two rows, so the pattern is a line of blocks plus frame hops
+    w = workload(1, mode="local3d", extra_tokens=extra, sink_range=128)
+    x = make_inputs(w)
+    _, sel, _ = run_and_check(w, x, range(w.H))
+    assert (sel["kept_cnt"] < w.N // 64).all()
+
+
+def test_local3d_bf16_n16k():
+    # 64 x 64 frames: one block per row, so the centre / +-1 frame / +-1 row stencil, plus sinks
+    w = workload(2, mode="local3d")
+    x = make_inputs(w, heads=[0, 7])
+    run_and_check(w, x, range(2))
+
+
+def test_local3d_bf16_q128_extra_dense_rows():
+    w = workload(3, mode="local3d", H=2, extra_tokens=256, dense_rows=(32768 - 1024, 32768))
+    x = make_inputs(w)
+    run_and_check(w, x, range(2), qblocks=_sample(60, n_sparse=48, n_dense=4))
+
+
+def test_local3d_bf16_frames_straddle_blocks():
+    # 45 x 80 frames (3600 tokens, not a whole number of 64-token blocks): the token-level rule
+    w = workload(2, mode="local3d", H=2, T=4, Hh=45, Ww=80, extra_tokens=128, sink_range=0)
+    x = make_inputs(w)
+    assert w.N % 64 == 0 and (w.Hh * w.Ww) % 64 != 0
+    run_and_check(w, x, range(2))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
