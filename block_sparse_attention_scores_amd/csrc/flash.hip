@@ -61,6 +61,7 @@ struct FlashSmem {
   __attribute__((aligned(16))) uint16_t k[2][64 * D];
   __attribute__((aligned(16))) uint16_t v[2][64 * D];
   __attribute__((aligned(16))) float bias[2][2][64];
+  __attribute__((aligned(16))) float zero[64];   // the bias of plain key tiles
 };
 
 struct TileDesc {
@@ -144,7 +145,10 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
   constexpr int TILE_BYTES = 64 * D * 2;
   int bh, pair;
   if (!flash_unit(P, G, blockIdx.x, &bh, &pair)) return;
-  const int tid = threadIdx.x, w = tid / 64, l = tid % 64, h32 = l / 32, c32 = l % 32;
+  // the wave index is uniform: read it into a scalar so that every per-wave decision (which
+  // query block, whether the wave works on a tile) is a scalar branch, not an exec mask
+  const int tid = threadIdx.x, l = tid % 64, h32 = l / 32, c32 = l % 32;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int g = w / WPQ;                     // this wave's query block within the pair
   const int b = bh / P.H, hh = bh % P.H;
   const uint16_t* Kb = static_cast<const uint16_t*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)hh * P.k.sh;
@@ -266,39 +270,10 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
       }
   };
 
-  // ---- one tile for this wave's 32 query rows; s holds the initial accumulators
-  auto compute = [&](int bf, f32x16_t* s) {
-    const char* kt_ = reinterpret_cast<const char*>(sm.k[bf]);
-    const char* vt_ = reinterpret_cast<const char*>(sm.v[bf]);
-    // S^T = K Q^T (+ bias); the K fragments of step ks+1 are read while step ks multiplies
-    bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kt_ + ak);
-    bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kt_ + ak + 32 * D * 2);
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      bf16x8_t n0 = a0, n1 = a1;
-      if (ks + 1 < D / 16) {
-        const uint32_t off = ak ^ (32u * (ks + 1));
-        n0 = *reinterpret_cast<const bf16x8_t*>(kt_ + off);
-        n1 = *reinterpret_cast<const bf16x8_t*>(kt_ + off + 32 * D * 2);
-      }
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s[1], 0, 0, 0);
-      a0 = n0;
-      a1 = n1;
-    }
-    __builtin_amdgcn_s_setprio(0);
-    // base-2 logits x = s * scale * log2(e); the max is taken on s (the scale is positive)
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx *= sl2;
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Lazy rescaling: the reference max moves (and the accumulator is rescaled) only when some
-    // row's max grows by more than 8 (base 2), so probabilities stay below 2^8 and most tiles
-    // skip the rescale.  The result is the same softmax, referenced to a different constant.
+  // Lazy rescaling: the reference max moves (and the accumulator is rescaled) only when some
+  // row's max grows by more than 8 (base 2), so probabilities stay below 2^8 and most steps skip
+  // the rescale.  The result is the same softmax, referenced to a different constant.
+  auto rescale = [&](float mx) {
     const float m_cand = fmaxf(m_run, mx);
     if (__any(m_cand > m_run + 8.f)) {
       const float m_new = m_cand == -__builtin_inff() ? m_run : m_cand;
@@ -310,13 +285,45 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
       m_run = m_new;
     }
-    const float nm = m_run == -__builtin_inff() ? 0.f : -m_run;
-    // O^T += V^T P^T, one 16-key step at a time.  The probabilities of step ks (registers
-    // 8(ks%2)..+8 of score half ks/2) are rounded to bf16 and summed (the sum sees the rounded
-    // values, as the product does).  Software pipeline: while the four products of step ks run
-    // on the matrix unit, the exponentials of step ks+1 run on the vector unit.
-    float psum = 0.f;
-    auto probs = [&](int ks) {
+  };
+  // Base-2 row max of one 32-key half of the scores (the scale is positive, so the max is
+  // taken on the raw scores).  Lanes l and l+32 hold the same rows, different keys.
+  auto half_max = [&](const f32x16_t& sh) {
+    float mx = sh[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sh[r]);
+    mx *= sl2;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  };
+
+  // ---- one tile for this wave's 32 query rows; s holds the tile's per-key biases (zeros for a
+  // plain key tile) and receives the scores.  The tile is two online-softmax steps of 32
+  // keys each, ordered so that the vector work of one half overlaps matrix work: the max of half
+  // 0 runs under the score products of half 1, the max of half 1 under the value products of
+  // half 0.  Within a half, the exponentials of one 16-key step overlap the products of the
+  // previous one.
+  auto compute = [&](int bf, f32x16_t* s) {
+    const char* kt_ = reinterpret_cast<const char*>(sm.k[bf]);
+    const char* vt_ = reinterpret_cast<const char*>(sm.v[bf]);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // S^T (keys 32kt..32kt+31) += K Q^T; K fragments of step ks+1 read during step ks
+      bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt_ + ak + kt * 32 * D * 2);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        bf16x8_t n = a;
+        if (ks + 1 < D / 16)
+          n = *reinterpret_cast<const bf16x8_t*>(kt_ + ((ak ^ (32u * (ks + 1))) + kt * 32 * D * 2));
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
+        a = n;
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // O^T += V^T P^T for one 16-key step ks; the probabilities (registers 8(ks%2)..+8 of half
+    // ks/2) are rounded to bf16 and summed as rounded, like the product sees them.
+    auto probs = [&](int ks, float nm, float& psum) {
       bf16x8_t pf;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -328,34 +335,35 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
       }
       return pf;
     };
-    bf16x8_t va[D / 32];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-      va[dt] = *reinterpret_cast<const bf16x8_t*>(vt_ + av + dt * 32 * 128);
-    bf16x8_t pcur = probs(0);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t vn[D / 32];
-      bf16x8_t pnext = pcur;
-      if (ks + 1 < 4) {
-        const uint32_t off = av ^ (32u * (ks + 1));
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          vn[dt] = *reinterpret_cast<const bf16x8_t*>(vt_ + off + dt * 32 * 128);
-        pnext = probs(ks + 1);
-      }
+    auto vread = [&](int ks, bf16x8_t* va) {
+      const uint32_t off = av ^ (32u * ks);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], pcur, o[dt], 0, 0, 0);
-      if (ks + 1 < 4) {
+        va[dt] = *reinterpret_cast<const bf16x8_t*>(vt_ + off + dt * 32 * 128);
+    };
+    float mx = half_max(s[0]);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) va[dt] = vn[dt];
-        pcur = pnext;
-      }
+    for (int kt = 0; kt < 2; ++kt) {
+      rescale(mx);
+      const float nm = m_run == -__builtin_inff() ? 0.f : -m_run;
+      float psum = 0.f;
+      bf16x8_t va[D / 32], vb[D / 32];
+      vread(2 * kt, va);
+      const bf16x8_t p0 = probs(2 * kt, nm, psum);
+      vread(2 * kt + 1, vb);
+      const bf16x8_t p1 = probs(2 * kt + 1, nm, psum);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], p0, o[dt], 0, 0, 0);
+      if (kt == 0) mx = half_max(s[1]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[dt], p1, o[dt], 0, 0, 0);
+      l_run += psum;
     }
-    l_run += psum;
   };
 
+  if (tid < 64) sm.zero[tid] = 0.f;       // visible after the first barrier of the loop
   TileDesc cur = it.next();
   int bf = 0;
   issue(cur, 0);
@@ -364,9 +372,7 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
     __syncthreads();
     const bool mine = wave_on && ((cur.sel >> g) & 1);
     f32x16_t s[2];
-    s[0] = f32x16_t{};
-    s[1] = f32x16_t{};
-    if (mine && cur.kind != 0) load_bias(sm.bias[bf][g], s);
+    if (mine) load_bias(cur.kind != 0 ? sm.bias[bf][g] : sm.zero, s);
     const TileDesc nxt = it.next();
     if (nxt.kind != 3) issue(nxt, bf ^ 1);
     if (mine) compute(bf, s);
