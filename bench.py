@@ -6,7 +6,11 @@ dense.  Inputs are seeded synthetic video-like latents (see gen/inputs.py) resid
 before timing starts.  One step = one whole forward call (pool, score, select, extra tokens,
 attention).  Prints one JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 4] [--heads H] [--mode M] [--no-cpu-baseline]
+
+--heads runs the workload with fewer heads (e.g. 3 of 24: one GPU's share when the heads are
+spread over eight GPUs); --mode times another selection mode (sol, sla, local3d) on the same
+inputs and grid.  Both change the workload named in the output line.
 """
 import argparse
 import json
@@ -69,6 +73,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, help="workload id (gen/inputs.py)")
     ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--heads", type=int, default=None, help="override the head count")
+    ap.add_argument("--mode", choices=("sol", "sla", "local3d"), default=None,
+                    help="override the selection mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
@@ -105,6 +112,8 @@ def cpu_baseline(w, x, heads=(0,), n_sparse=24, n_dense=4, seed=7):
         cores = 1
     p = dict(block_q=w.block_q, block_k=w.block_k, tau=w.tau, keep_percent=w.keep_percent,
              sink_range=w.sink_range, extra_tokens=w.extra_tokens, dense_rows=w.dense_rows)
+    if w.mode == "local3d":
+        p["grid"] = (w.T, w.Hh, w.Ww)
     t_sel = []
     t_sparse, t_dense = [], []
     rng = np.random.default_rng(seed)
@@ -153,9 +162,19 @@ def main():
     import block_sparse_attention_scores_amd as sa
     from gen import make_inputs, workload
 
-    w = workload(a.config)
+    ov = {}
     if a.tau is not None:
-        w = workload(a.config, tau=a.tau)
+        ov["tau"] = a.tau
+    if a.heads is not None:
+        if a.heads < 1:
+            raise SystemExit("--heads must be >= 1")
+        ov["H"] = a.heads
+    if a.mode is not None:
+        ov["mode"] = a.mode
+    w = workload(a.config, **ov)
+    if ov:
+        tag = "".join(f"-{k}{v}" for k, v in sorted(ov.items()))
+        w = workload(a.config, name=w.name + tag, **ov)
     dev = torch.device("cuda:0")
     log(f"[bench] generating {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}")
     t0 = time.perf_counter()
@@ -166,7 +185,7 @@ def main():
         q, k, v = to(x.q_bits), to(x.k_bits), to(x.v_bits)
     else:
         q, k, v = (torch.from_numpy(t).to(dev) for t in (x.q, x.k, x.v))
-    mode = sa.MODE_SOL if w.mode == "sol" else sa.MODE_SLA
+    mode = {"sol": sa.MODE_SOL, "sla": sa.MODE_SLA, "local3d": sa.MODE_LOCAL3D}[w.mode]
     out = torch.empty_like(q)
     ws = sa.alloc_workspace(mode, q, w.block_q, w.block_k)
 
@@ -175,6 +194,11 @@ def main():
             sa.sol_attn(q, k, v, tau=w.tau, block_q=w.block_q, block_k=w.block_k,
                         sink_range=w.sink_range, extra_tokens=w.extra_tokens,
                         dense_rows=w.dense_rows, out=out, workspace=ws)
+        elif w.mode == "local3d":
+            sa.local3d_attn(q, k, v, grid=(w.T, w.Hh, w.Ww), block_q=w.block_q,
+                            block_k=w.block_k, sink_range=w.sink_range,
+                            extra_tokens=w.extra_tokens, dense_rows=w.dense_rows, out=out,
+                            workspace=ws)
         else:
             sa.sla_attn(q, k, v, keep_percent=w.keep_percent, block_q=w.block_q,
                         block_k=w.block_k, sink_range=w.sink_range,
@@ -189,13 +213,17 @@ def main():
     sa.timing_read()                 # drop anything recorded before
     sa.timing_enable(True)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
-    for _ in range(a.steps):
+    marks[0].record()
+    for i in range(a.steps):
         step()
+        marks[i + 1].record()
     end.record()
     torch.cuda.synchronize()
+    per_call = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(a.steps)])
     t_wall = time.perf_counter() - t_wall
     sa.timing_enable(False)
     per_kernel = sa.timing_read()
@@ -273,6 +301,9 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms_per_call, 4),
+        "ms_per_call_median": round(float(np.median(per_call)), 4),
+        "ms_per_call_p10": round(float(np.percentile(per_call, 10)), 4),
+        "ms_per_call_p90": round(float(np.percentile(per_call, 90)), 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
