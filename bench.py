@@ -239,6 +239,24 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy calibration: 3 x 1 GiB device copies")
 
+    # one more (untimed) call with the library's per-call counters
+    stats_t = torch.zeros(sa.NSTATS, dtype=torch.int64, device=dev)
+    if w.mode == "sol":
+        sa.sol_attn(q, k, v, tau=w.tau, block_q=w.block_q, block_k=w.block_k,
+                    sink_range=w.sink_range, extra_tokens=w.extra_tokens, dense_rows=w.dense_rows,
+                    out=out, workspace=ws, stats=stats_t, flags=sa.FLAG_CHECK_FINITE)
+    elif w.mode == "local3d":
+        sa.local3d_attn(q, k, v, grid=(w.T, w.Hh, w.Ww), block_q=w.block_q, block_k=w.block_k,
+                        sink_range=w.sink_range, extra_tokens=w.extra_tokens,
+                        dense_rows=w.dense_rows, out=out, workspace=ws, stats=stats_t,
+                        flags=sa.FLAG_CHECK_FINITE)
+    else:
+        sa.sla_attn(q, k, v, keep_percent=w.keep_percent, block_q=w.block_q, block_k=w.block_k,
+                    sink_range=w.sink_range, extra_tokens=w.extra_tokens, dense_rows=w.dense_rows,
+                    out=out, workspace=ws, stats=stats_t, flags=sa.FLAG_CHECK_FINITE)
+    torch.cuda.synchronize()
+    call_stats = dict(zip(sa.STAT_NAMES, (int(x_) for x_ in stats_t.cpu().tolist())))
+
     views = sa.selection_views(ws, mode, sa.BF16 if w.dtype == "bf16" else sa.FP32, w.B, w.H, w.N,
                                w.d, w.block_q, w.block_k)
     sel = {k_: v_.cpu().numpy() for k_, v_ in views.items()}
@@ -322,6 +340,7 @@ def main():
         "exact_tflop": round(f_exact / 1e12, 4),
         "centroid_tflop": round(f_cent / 1e12, 4),
         "kernels": kern,
+        "call_stats": call_stats,
     }
     print(json.dumps(res), flush=True)
 

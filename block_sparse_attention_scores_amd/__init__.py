@@ -5,7 +5,7 @@ The compute path is libsolattn, hand-written HIP for gfx950 behind a C ABI
 """
 from ._lib import (  # noqa: F401
     BF16, FP32, MODE_SOL, MODE_SLA, MODE_LOCAL3D, MAX_EXTRA, OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP,
-    FLAG_EXACT_EXTRA,
+    FLAG_EXACT_EXTRA, FLAG_CHECK_FINITE, NSTATS, STAT_NAMES,
     SolattnError, Opts, WsLayout, lib, sol_attn, sla_attn, local3d_attn, workspace_layout, workspace_bytes,
     alloc_workspace, selection_views, status_string, last_error, kernel_names, timing_enable,
     timing_read, make_opts, header_functions,

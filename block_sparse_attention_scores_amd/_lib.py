@@ -28,6 +28,10 @@ class SolattnError(RuntimeError):
 
 
 FLAG_EXACT_EXTRA = 1   # SOLATTN_FLAG_EXACT_EXTRA
+FLAG_CHECK_FINITE = 2  # SOLATTN_FLAG_CHECK_FINITE
+NSTATS = 8             # SOLATTN_NSTATS
+STAT_NAMES = ("kept_blocks", "selected_qblocks", "exact_pairs", "centroid_terms", "extra_tokens",
+              "near_threshold", "exact_extra_qblocks", "nonfinite")
 
 
 class Opts(ctypes.Structure):
@@ -44,6 +48,7 @@ class Opts(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("flags", ctypes.c_uint),
+        ("stats", ctypes.c_void_p),
     ]
 
 
@@ -120,7 +125,7 @@ def workspace_bytes(mode, dtype, B, H, N, d, block_q, block_k) -> int:
 
 
 def make_opts(dtype=BF16, strides=None, dense_rows=(0, 0), workspace=0, workspace_bytes=0,
-              stream=0, flags=0) -> Opts:
+              stream=0, flags=0, stats=0) -> Opts:
     o = Opts()
     o.struct_size = ctypes.sizeof(Opts)
     o.dtype = dtype
@@ -134,6 +139,7 @@ def make_opts(dtype=BF16, strides=None, dense_rows=(0, 0), workspace=0, workspac
     o.workspace_bytes = int(workspace_bytes)
     o.stream = stream or None
     o.flags = int(flags)
+    o.stats = stats or None
     return o
 
 
@@ -186,7 +192,7 @@ def alloc_workspace(mode, q, block_q, block_k):
 
 
 def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, extra_tokens,
-          dense_rows, out, workspace, stream, flags=0, grid=None):
+          dense_rows, out, workspace, stream, flags=0, grid=None, stats=None):
     torch = _torch()
     B, H, N, d = q.shape
     for n, t in (("k", k), ("v", v)):
@@ -200,8 +206,13 @@ def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, ext
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     strides = [tuple(t.stride()[:3]) for t in (q, k, v, out)]
+    if stats is not None:
+        if not stats.is_cuda or stats.dtype != torch.int64 or stats.numel() < NSTATS \
+                or not stats.is_contiguous():
+            raise ValueError(f"stats must be a contiguous int64 GPU tensor of >= {NSTATS} elements")
     opts = make_opts(_dtype_code(q), strides, dense_rows, workspace.data_ptr(),
-                     workspace.numel() * workspace.element_size(), stream, flags)
+                     workspace.numel() * workspace.element_size(), stream, flags,
+                     stats.data_ptr() if stats is not None else 0)
     L = lib()
     if mode == MODE_SOL:
         rc = L.sol_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
@@ -222,27 +233,29 @@ def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, ext
 
 def sol_attn(q, k, v, *, tau=1.3, block_q=64, block_k=64, sink_range=0, extra_tokens=0,
              dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False,
-             flags=0):
-    """sol-attn forward on [B, H, N, d] GPU tensors (bfloat16 or float32); see include/solattn.h."""
+             flags=0, stats=None):
+    """sol-attn forward on [B, H, N, d] GPU tensors (bfloat16 or float32); see include/solattn.h.
+    stats: optional int64 GPU tensor of NSTATS elements for the per-call counters."""
     o, ws = _call(MODE_SOL, q, k, v, tau=tau, keep_percent=0.0, block_q=block_q, block_k=block_k,
                   sink_range=sink_range, extra_tokens=extra_tokens, dense_rows=dense_rows, out=out,
-                  workspace=workspace, stream=stream, flags=flags)
+                  workspace=workspace, stream=stream, flags=flags, stats=stats)
     return (o, ws) if return_workspace else o
 
 
 def sla_attn(q, k, v, *, keep_percent=10.0, block_q=128, block_k=64, sink_range=0, extra_tokens=0,
              dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False,
-             flags=0):
+             flags=0, stats=None):
     """sla forward on [B, H, N, d] GPU tensors (bfloat16 or float32); see include/solattn.h."""
     o, ws = _call(MODE_SLA, q, k, v, tau=0.0, keep_percent=keep_percent, block_q=block_q,
                   block_k=block_k, sink_range=sink_range, extra_tokens=extra_tokens,
-                  dense_rows=dense_rows, out=out, workspace=workspace, stream=stream, flags=flags)
+                  dense_rows=dense_rows, out=out, workspace=workspace, stream=stream, flags=flags,
+                  stats=stats)
     return (o, ws) if return_workspace else o
 
 
 def local3d_attn(q, k, v, *, grid, block_q=64, block_k=64, sink_range=0, extra_tokens=0,
                  dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False,
-                 flags=0):
+                 flags=0, stats=None):
     """Static local 3-D neighbourhood forward on [B, H, N, d] GPU tensors; grid = (frames,
     height, width) with frames*height*width == N; see include/solattn.h."""
     if len(grid) != 3:
@@ -250,7 +263,7 @@ def local3d_attn(q, k, v, *, grid, block_q=64, block_k=64, sink_range=0, extra_t
     o, ws = _call(MODE_LOCAL3D, q, k, v, tau=0.0, keep_percent=100.0, block_q=block_q,
                   block_k=block_k, sink_range=sink_range, extra_tokens=extra_tokens,
                   dense_rows=dense_rows, out=out, workspace=workspace, stream=stream, flags=flags,
-                  grid=grid)
+                  grid=grid, stats=stats)
     return (o, ws) if return_workspace else o
 
 

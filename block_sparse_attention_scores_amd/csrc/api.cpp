@@ -80,6 +80,13 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   if (sink_range < 0 || sink_range > N) return fail(SOLATTN_EINVAL, "sink_range %d outside [0, N]", sink_range);
   const int d0 = opts ? opts->dense_row_begin : 0, d1 = opts ? opts->dense_row_end : 0;
   if (d0 < 0 || d1 < d0 || d1 > N) return fail(SOLATTN_EINVAL, "dense rows [%d, %d) outside [0, N]", d0, d1);
+  const unsigned flags = opts ? opts->flags : 0u;
+  if (flags & ~(SOLATTN_FLAG_EXACT_EXTRA | SOLATTN_FLAG_CHECK_FINITE))
+    return fail(SOLATTN_EINVAL, "unknown flags 0x%x", flags);
+  if ((flags & SOLATTN_FLAG_CHECK_FINITE) && !(opts && opts->stats))
+    return fail(SOLATTN_EINVAL, "SOLATTN_FLAG_CHECK_FINITE needs opts->stats");
+  if (opts && opts->stats && reinterpret_cast<uintptr_t>(opts->stats) % 8)
+    return fail(SOLATTN_EINVAL, "stats not 8-byte aligned");
 
   const int64_t zero[3] = {0, 0, 0};
   st[0] = resolve(opts ? opts->q_stride : zero, H, N, d);
@@ -283,6 +290,9 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
     P.v_t = reinterpret_cast<uint16_t*>(ws + L.v_t);
   }
 
+  if (opts && opts->stats && L.extra_part - L.extra_buf < solattn::stats_scratch_bytes())
+    return fail(SOLATTN_ENOTSUP, "stats: candidate buffer smaller than the counters' scratch");
+
   std::unique_lock<std::mutex> tl(g_t_mu);
   const bool timing = g_timing;
   TimedCall tc;
@@ -331,6 +341,11 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
     if ((err = solattn::launch_sparse_flash(P, stream)) != hipSuccess) return "sparse_flash_fwd";
     tc.ran[4] = true;
     mark(5);
+    if (opts && opts->stats) {
+      const int fin = (opts->flags & SOLATTN_FLAG_CHECK_FINITE) ? 1 : 0;
+      if ((err = solattn::launch_stats(P, reinterpret_cast<long long*>(opts->stats), fin, stream)) != hipSuccess)
+        return "stats";
+    }
     return nullptr;
   };
   if (const char* failed = launch_all()) {

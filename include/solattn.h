@@ -74,6 +74,7 @@ typedef struct solattn_opts {
   size_t workspace_bytes;         /* its size; must be >= solattn_workspace_bytes(...)     */
   void*  stream;                  /* hipStream_t; NULL = null stream                       */
   unsigned flags;                 /* SOLATTN_FLAG_* bits; 0 = defaults                       */
+  int64_t* stats;                 /* device int64[SOLATTN_NSTATS] for per-call counters, or NULL */
 } solattn_opts;
 
 /*
@@ -84,6 +85,31 @@ typedef struct solattn_opts {
  * to exercise and check the exact pass on any input.
  */
 #define SOLATTN_FLAG_EXACT_EXTRA 1u
+
+/*
+ * SOLATTN_FLAG_CHECK_FINITE: also count the NaN and infinite values of q, k, v and out into
+ * stats[7] (one extra pass over the four tensors).  Needs opts->stats; without it the call
+ * returns SOLATTN_EINVAL.
+ */
+#define SOLATTN_FLAG_CHECK_FINITE 2u
+
+/*
+ * Per-call counters (opts->stats != NULL): a device array of SOLATTN_NSTATS int64 values,
+ * 8-byte aligned, overwritten asynchronously on the call's stream after the attention (not
+ * covered by the per-kernel timing).  Sums over every (batch, head):
+ *   [0] kept key blocks of the query blocks that run selection (not dense-row blocks)
+ *   [1] query blocks that run selection
+ *   [2] exact (query row, key) pairs: kept-block and extra tokens, every key for dense rows
+ *   [3] centroid terms (query row, key block): sol-attn only
+ *   [4] extra tokens used
+ *   [5] key blocks whose score lies within 1e-4 standard deviations of the sol-attn threshold
+ *       (recomputed in fp32; a measure of how close the selection is to flipping; 0 for sla,
+ *       the local 3-D pattern and tau = -inf)
+ *   [6] query blocks whose extra tokens the exact pass selected (see SOLATTN_FLAG_EXACT_EXTRA)
+ *   [7] non-finite values among q, k, v and out with SOLATTN_FLAG_CHECK_FINITE, else -1
+ * The counters are computed with a fixed reduction order, so they do not vary between runs.
+ */
+#define SOLATTN_NSTATS 8
 
 /*
  * sol-attn forward.
@@ -176,7 +202,8 @@ int local3d_check_args(const void* q, const void* k, const void* v, void* out,
  *   extra_cnt int32 [B*H, Mq]      number of extra tokens
  *   extra_idx int32 [B*H, Mq, 256] extra token indices, ascending, first extra_cnt valid
  *   extra_buf, extra_part: scratch of the extra-token selection (candidate lists per query
- *             block, token slice and wave, and their lengths)
+ *             block, token slice and wave, and their lengths); extra_buf also holds the
+ *             partial sums of the per-call counters when they are requested
  *   extra_flag int32 [B*H, Mq]     1 where the extra-token selection's first pass, whose
  *             threshold is seeded from a sample of the keys, kept fewer candidates than the
  *             selection needs, so that the query block was selected again with every

@@ -113,6 +113,17 @@ def test_local3d_validation():
     assert rc == sa.EINVAL and "grid" in sa.last_error()
 
 
+def test_stats_and_flag_validation():
+    assert check(opts=sa.make_opts(stats=1 << 33)) == sa.OK
+    assert check(opts=sa.make_opts(stats=1 << 33, flags=sa.FLAG_CHECK_FINITE)) == sa.OK
+    assert check(opts=sa.make_opts(flags=sa.FLAG_CHECK_FINITE)) == sa.EINVAL
+    assert "stats" in sa.last_error()
+    assert check(opts=sa.make_opts(stats=(1 << 33) + 4)) == sa.EINVAL
+    assert check(opts=sa.make_opts(flags=4)) == sa.EINVAL
+    assert "flags" in sa.last_error()
+    assert check(opts=sa.make_opts(flags=sa.FLAG_EXACT_EXTRA | sa.FLAG_CHECK_FINITE, stats=1 << 33)) == sa.OK
+
+
 def test_page_parameter_ranges_are_accepted():
     g = json.load(open(GOLDEN))
     assert check(extra=g["extra_tokens_range"]["max"]) == sa.OK

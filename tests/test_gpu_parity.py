@@ -225,3 +225,85 @@ def test_library_errors_raise():
     with pytest.raises(sa.SolattnError) as e:
         sa.sol_attn(q, k, v, workspace=ws)
     assert e.value.status == sa.EWORKSPACE
+
+
+def _host_counters(sel, mode, B, H, Mq, M, bq, bk, N, dense_rows, extra_tokens, tau):
+    kept = sel["kept_cnt"].astype(np.int64)
+    extra = sel["extra_cnt"].astype(np.int64)
+    dense = np.zeros(Mq, dtype=bool)
+    dense[dense_rows[0] // bq:dense_rows[1] // bq] = True
+    sp = ~dense
+    c = np.zeros(8, dtype=np.int64)
+    c[0] = kept[:, sp].sum()
+    c[1] = B * H * sp.sum()
+    c[2] = (bq * (kept[:, sp] * bk + extra[:, sp])).sum() + B * H * dense.sum() * bq * N
+    if mode == "sol":
+        c[3] = bq * (sel["mult"][:, sp, :M] > 0).sum()
+    c[4] = extra[:, sp].sum()
+    if extra_tokens > 0 and tau != -math.inf:
+        c[6] = (sel["extra_flag"][:, sp] == 1).sum()
+    return c
+
+
+@pytest.mark.parametrize("mode", ["sol", "sla", "local3d"])
+def test_call_counters(mode):
+    # the per-call counters against recounts from the call's own selection lists
+    w = workload(2, mode=mode, H=2, extra_tokens=128, dense_rows=(16384 - 1024, 16384),
+                 block_q=128 if mode == "sla" else 64, keep_percent=15.0)
+    x = make_inputs(w)
+    q, k, v = device_inputs(x)
+    stats = torch.zeros(sa.NSTATS, dtype=torch.int64, device="cuda")
+    print(f"\n[counters] mode={mode} N={w.N}", flush=True)
+    kw = dict(block_q=w.block_q, block_k=64, sink_range=w.sink_range, extra_tokens=w.extra_tokens,
+              dense_rows=w.dense_rows, return_workspace=True, stats=stats)
+    if mode == "sol":
+        out, ws = sa.sol_attn(q, k, v, tau=w.tau, **kw)
+    elif mode == "sla":
+        out, ws = sa.sla_attn(q, k, v, keep_percent=w.keep_percent, **kw)
+    else:
+        out, ws = sa.local3d_attn(q, k, v, grid=(w.T, w.Hh, w.Ww), **kw)
+    torch.cuda.synchronize()
+    m = {"sol": sa.MODE_SOL, "sla": sa.MODE_SLA, "local3d": sa.MODE_LOCAL3D}[mode]
+    views = sa.selection_views(ws, m, sa.BF16, 1, w.H, w.N, w.d, w.block_q, 64)
+    sel = {k_: v_.cpu().numpy() for k_, v_ in views.items()}
+    got = stats.cpu().numpy()
+    Mq, M = w.N // w.block_q, w.N // 64
+    ref = _host_counters(sel, mode, 1, w.H, Mq, M, w.block_q, 64, w.N, w.dense_rows,
+                         w.extra_tokens, w.tau)
+    print(f"[counters] {dict(zip(sa.STAT_NAMES, got.tolist()))}", flush=True)
+    for idx in (0, 1, 2, 3, 4, 6):
+        assert got[idx] == ref[idx], (sa.STAT_NAMES[idx], got[idx], ref[idx])
+    assert got[7] == -1
+    if mode == "sol":
+        # near-threshold blocks, recounted in fp64 from the call's scores (a diagnostic: the two
+        # may differ on a block that sits exactly at the band's edge)
+        s_ = sel["scores"].astype(np.float64)
+        dense = np.zeros(Mq, dtype=bool)
+        dense[w.dense_rows[0] // 64:w.dense_rows[1] // 64] = True
+        s_ = s_[:, ~dense]
+        mu = s_.mean(axis=2, keepdims=True)
+        sd = s_.std(axis=2, keepdims=True)
+        near = int((np.abs(s_ - (mu + w.tau * sd)) <= 1e-4 * sd).sum())
+        assert abs(int(got[5]) - near) <= max(2, near // 10), (got[5], near)
+    else:
+        assert got[5] == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_finite_check_counts_nonfinite_values(dtype):
+    x = random_qkv(1, 2, 2048, 64, seed=9, dtype=dtype)
+    q, k, v = device_inputs(x)
+    stats = torch.zeros(sa.NSTATS, dtype=torch.int64, device="cuda")
+    print(f"\n[finite] dtype={dtype} clean", flush=True)
+    sa.sol_attn(q, k, v, tau=1.3, stats=stats, flags=sa.FLAG_CHECK_FINITE)
+    torch.cuda.synchronize()
+    assert stats[7].item() == 0
+    q[0, 0, 5, 3] = float("inf")
+    k[0, 1, 100, 7] = float("nan")
+    v[0, 1, 2000, 0] = float("-inf")
+    print(f"[finite] dtype={dtype} with three non-finite inputs", flush=True)
+    out = sa.sol_attn(q, k, v, tau=1.3, stats=stats, flags=sa.FLAG_CHECK_FINITE)
+    torch.cuda.synchronize()
+    n_out = int((~torch.isfinite(out.float())).sum().item())
+    assert n_out > 0
+    assert stats[7].item() == 3 + n_out
