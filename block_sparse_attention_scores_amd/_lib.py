@@ -49,6 +49,8 @@ class Opts(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("flags", ctypes.c_uint),
         ("stats", ctypes.c_void_p),
+        ("q_row_begin", ctypes.c_int),
+        ("q_row_end", ctypes.c_int),
     ]
 
 
@@ -85,6 +87,10 @@ def lib() -> ctypes.CDLL:
     L.solattn_workspace_layout.restype = i
     L.solattn_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
     L.solattn_workspace_bytes.restype = ctypes.c_size_t
+    L.solattn_workspace_layout_rows.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(WsLayout)]
+    L.solattn_workspace_layout_rows.restype = i
+    L.solattn_workspace_bytes_rows.argtypes = [i, i, i, i, i, i, i, i, i]
+    L.solattn_workspace_bytes_rows.restype = ctypes.c_size_t
     L.solattn_status_string.argtypes = [i]
     L.solattn_status_string.restype = ctypes.c_char_p
     L.solattn_last_error.argtypes = []
@@ -112,20 +118,24 @@ def kernel_names():
 
 
 def workspace_layout(mode: int, dtype: int, B: int, H: int, N: int, d: int, block_q: int,
-                     block_k: int) -> WsLayout:
+                     block_k: int, q_rows: int | None = None) -> WsLayout:
+    """Offsets of the intermediate buffers; q_rows: rows of a query-row window (default N)."""
     L = WsLayout()
-    rc = lib().solattn_workspace_layout(mode, dtype, B, H, N, d, block_q, block_k, ctypes.byref(L))
+    rows = N if q_rows is None else int(q_rows)
+    rc = lib().solattn_workspace_layout_rows(mode, dtype, B, H, N, d, block_q, block_k, rows,
+                                             ctypes.byref(L))
     if rc != OK:
         raise SolattnError(rc, "invalid workspace shape")
     return L
 
 
-def workspace_bytes(mode, dtype, B, H, N, d, block_q, block_k) -> int:
-    return int(lib().solattn_workspace_bytes(mode, dtype, B, H, N, d, block_q, block_k))
+def workspace_bytes(mode, dtype, B, H, N, d, block_q, block_k, q_rows=None) -> int:
+    rows = N if q_rows is None else int(q_rows)
+    return int(lib().solattn_workspace_bytes_rows(mode, dtype, B, H, N, d, block_q, block_k, rows))
 
 
 def make_opts(dtype=BF16, strides=None, dense_rows=(0, 0), workspace=0, workspace_bytes=0,
-              stream=0, flags=0, stats=0) -> Opts:
+              stream=0, flags=0, stats=0, q_rows=None) -> Opts:
     o = Opts()
     o.struct_size = ctypes.sizeof(Opts)
     o.dtype = dtype
@@ -140,6 +150,8 @@ def make_opts(dtype=BF16, strides=None, dense_rows=(0, 0), workspace=0, workspac
     o.stream = stream or None
     o.flags = int(flags)
     o.stats = stats or None
+    if q_rows is not None:
+        o.q_row_begin, o.q_row_end = int(q_rows[0]), int(q_rows[1])
     return o
 
 
@@ -184,15 +196,17 @@ def _check_tensor(name, t, shape, dtype):
         raise ValueError(f"{name}: the d axis must be contiguous")
 
 
-def alloc_workspace(mode, q, block_q, block_k):
+def alloc_workspace(mode, q, block_q, block_k, q_rows=None):
+    """A workspace for a call on q's shape (or on the query-row window q_rows = (begin, end))."""
     torch = _torch()
     B, H, N, d = q.shape
-    nbytes = workspace_bytes(mode, _dtype_code(q), B, H, N, d, block_q, block_k)
+    rows = None if q_rows is None else q_rows[1] - q_rows[0]
+    nbytes = workspace_bytes(mode, _dtype_code(q), B, H, N, d, block_q, block_k, rows)
     return torch.empty(nbytes, dtype=torch.uint8, device=q.device)
 
 
 def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, extra_tokens,
-          dense_rows, out, workspace, stream, flags=0, grid=None, stats=None):
+          dense_rows, out, workspace, stream, flags=0, grid=None, stats=None, q_rows=None):
     torch = _torch()
     B, H, N, d = q.shape
     for n, t in (("k", k), ("v", v)):
@@ -202,7 +216,7 @@ def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, ext
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     _check_tensor("out", out, q.shape, q.dtype)
     if workspace is None:
-        workspace = alloc_workspace(mode, q, block_q, block_k)
+        workspace = alloc_workspace(mode, q, block_q, block_k, q_rows)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     strides = [tuple(t.stride()[:3]) for t in (q, k, v, out)]
@@ -212,7 +226,7 @@ def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, ext
             raise ValueError(f"stats must be a contiguous int64 GPU tensor of >= {NSTATS} elements")
     opts = make_opts(_dtype_code(q), strides, dense_rows, workspace.data_ptr(),
                      workspace.numel() * workspace.element_size(), stream, flags,
-                     stats.data_ptr() if stats is not None else 0)
+                     stats.data_ptr() if stats is not None else 0, q_rows)
     L = lib()
     if mode == MODE_SOL:
         rc = L.sol_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
@@ -233,29 +247,30 @@ def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, ext
 
 def sol_attn(q, k, v, *, tau=1.3, block_q=64, block_k=64, sink_range=0, extra_tokens=0,
              dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False,
-             flags=0, stats=None):
+             flags=0, stats=None, q_rows=None):
     """sol-attn forward on [B, H, N, d] GPU tensors (bfloat16 or float32); see include/solattn.h.
-    stats: optional int64 GPU tensor of NSTATS elements for the per-call counters."""
+    stats: optional int64 GPU tensor of NSTATS elements for the per-call counters; q_rows:
+    optional (begin, end) query-row window (only those rows of out are written)."""
     o, ws = _call(MODE_SOL, q, k, v, tau=tau, keep_percent=0.0, block_q=block_q, block_k=block_k,
                   sink_range=sink_range, extra_tokens=extra_tokens, dense_rows=dense_rows, out=out,
-                  workspace=workspace, stream=stream, flags=flags, stats=stats)
+                  workspace=workspace, stream=stream, flags=flags, stats=stats, q_rows=q_rows)
     return (o, ws) if return_workspace else o
 
 
 def sla_attn(q, k, v, *, keep_percent=10.0, block_q=128, block_k=64, sink_range=0, extra_tokens=0,
              dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False,
-             flags=0, stats=None):
+             flags=0, stats=None, q_rows=None):
     """sla forward on [B, H, N, d] GPU tensors (bfloat16 or float32); see include/solattn.h."""
     o, ws = _call(MODE_SLA, q, k, v, tau=0.0, keep_percent=keep_percent, block_q=block_q,
                   block_k=block_k, sink_range=sink_range, extra_tokens=extra_tokens,
                   dense_rows=dense_rows, out=out, workspace=workspace, stream=stream, flags=flags,
-                  stats=stats)
+                  stats=stats, q_rows=q_rows)
     return (o, ws) if return_workspace else o
 
 
 def local3d_attn(q, k, v, *, grid, block_q=64, block_k=64, sink_range=0, extra_tokens=0,
                  dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False,
-                 flags=0, stats=None):
+                 flags=0, stats=None, q_rows=None):
     """Static local 3-D neighbourhood forward on [B, H, N, d] GPU tensors; grid = (frames,
     height, width) with frames*height*width == N; see include/solattn.h."""
     if len(grid) != 3:
@@ -263,14 +278,16 @@ def local3d_attn(q, k, v, *, grid, block_q=64, block_k=64, sink_range=0, extra_t
     o, ws = _call(MODE_LOCAL3D, q, k, v, tau=0.0, keep_percent=100.0, block_q=block_q,
                   block_k=block_k, sink_range=sink_range, extra_tokens=extra_tokens,
                   dense_rows=dense_rows, out=out, workspace=workspace, stream=stream, flags=flags,
-                  grid=grid, stats=stats)
+                  grid=grid, stats=stats, q_rows=q_rows)
     return (o, ws) if return_workspace else o
 
 
-def selection_views(workspace, mode, dtype, B, H, N, d, block_q, block_k):
-    """Views of a call's intermediate results inside its workspace tensor (torch, on device)."""
+def selection_views(workspace, mode, dtype, B, H, N, d, block_q, block_k, q_rows=None):
+    """Views of a call's intermediate results inside its workspace tensor (torch, on device);
+    q_rows = (begin, end) for a call on a query-row window (its query blocks count from 0)."""
     torch = _torch()
-    L = workspace_layout(mode, dtype, B, H, N, d, block_q, block_k)
+    L = workspace_layout(mode, dtype, B, H, N, d, block_q, block_k,
+                         None if q_rows is None else q_rows[1] - q_rows[0])
     BH, Mq, M, Mpad = B * H, L.Mq, L.M, L.Mpad
 
     def view(off, count, dt, shape):

@@ -4,6 +4,7 @@
 // needs no block scores and skips block_score.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -80,6 +81,9 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   if (sink_range < 0 || sink_range > N) return fail(SOLATTN_EINVAL, "sink_range %d outside [0, N]", sink_range);
   const int d0 = opts ? opts->dense_row_begin : 0, d1 = opts ? opts->dense_row_end : 0;
   if (d0 < 0 || d1 < d0 || d1 > N) return fail(SOLATTN_EINVAL, "dense rows [%d, %d) outside [0, N]", d0, d1);
+  const int r0 = opts ? opts->q_row_begin : 0, r1 = opts ? opts->q_row_end : 0;
+  if (!(r0 == 0 && r1 == 0) && !(r0 >= 0 && r0 < r1 && r1 <= N))
+    return fail(SOLATTN_EINVAL, "query-row window [%d, %d) not inside [0, N]", r0, r1);
   const unsigned flags = opts ? opts->flags : 0u;
   if (flags & ~(SOLATTN_FLAG_EXACT_EXTRA | SOLATTN_FLAG_CHECK_FINITE))
     return fail(SOLATTN_EINVAL, "unknown flags 0x%x", flags);
@@ -113,6 +117,7 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   if (block_q != 64 && block_q != 128) return fail(SOLATTN_ENOTSUP, "block_q=%d (this build: 64, 128)", block_q);
   if (N % block_q || N % block_k) return fail(SOLATTN_ENOTSUP, "N=%d not a multiple of the block sizes", N);
   if (d0 % block_q || d1 % block_q) return fail(SOLATTN_ENOTSUP, "dense rows not block_q aligned");
+  if (r0 % block_q || r1 % block_q) return fail(SOLATTN_ENOTSUP, "query-row window not block_q aligned");
   if ((int64_t)B * H > 65535) return fail(SOLATTN_ENOTSUP, "B*H=%lld too large", (long long)B * H);
   if (dtype == SOLATTN_BF16 && N / block_k > solattn::MAX_BLOCKS_BF16)
     return fail(SOLATTN_ENOTSUP, "bf16: more than %d key blocks", solattn::MAX_BLOCKS_BF16);
@@ -129,14 +134,16 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   return SOLATTN_OK;
 }
 
-int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k, solattn_ws_layout* L) {
+// q_rows: query rows of the computed window (N for the whole sequence).
+int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k, solattn_ws_layout* L,
+           int q_rows) {
   (void)mode;
-  if (B < 1 || H < 1 || N < 1 || d < 1 || block_q < 1 || block_k < 1 ||
+  if (B < 1 || H < 1 || N < 1 || d < 1 || block_q < 1 || block_k < 1 || q_rows < 1 || q_rows > N ||
       (dtype != SOLATTN_BF16 && dtype != SOLATTN_FP32))
     return SOLATTN_EINVAL;
   std::memset(L, 0, sizeof *L);
   const size_t BH = (size_t)B * H;
-  const int Mq = (N + block_q - 1) / block_q, M = (N + block_k - 1) / block_k;
+  const int Mq = (q_rows + block_q - 1) / block_q, M = (N + block_k - 1) / block_k;
   const int Mpad = (M + 63) / 64 * 64;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -211,8 +218,10 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
                  extra_tokens, opts, st, grid);
   if (rc != SOLATTN_OK) return rc;
   const int dtype = opts ? opts->dtype : SOLATTN_BF16;
+  int r0 = opts ? opts->q_row_begin : 0, r1 = opts ? opts->q_row_end : 0;
+  if (r0 == 0 && r1 == 0) r1 = N;
   solattn_ws_layout L;
-  layout(mode, dtype, B, H, N, d, block_q, block_k, &L);
+  layout(mode, dtype, B, H, N, d, block_q, block_k, &L, r1 - r0);
   hipStream_t stream = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
 
   char* ws = nullptr;
@@ -259,9 +268,11 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   P.sink_blocks = (sink_range + block_k - 1) / block_k;
   P.extra = extra_tokens;
   P.exact_extra = (opts && (opts->flags & SOLATTN_FLAG_EXACT_EXTRA)) ? 1 : 0;
+  P.q0 = r0 / block_q;
+  // the dense range, intersected with the window, in window-local query blocks
   const int d0 = opts ? opts->dense_row_begin : 0, d1 = opts ? opts->dense_row_end : 0;
-  P.dense_q0 = d0 / block_q;
-  P.dense_q1 = d1 / block_q;
+  P.dense_q0 = std::max(d0, r0) / block_q - P.q0;
+  P.dense_q1 = std::min(d1, r1) / block_q - P.q0;
   if (P.dense_q1 <= P.dense_q0) P.dense_q0 = P.dense_q1 = 0;
   P.frames = grid[0]; P.height = grid[1]; P.width = grid[2];
   P.scale = 1.0f / std::sqrt(static_cast<float>(d));
@@ -411,12 +422,25 @@ int local3d_check_args(const void* q, const void* k, const void* v, void* out, i
 int solattn_workspace_layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k,
                              solattn_ws_layout* out) {
   if (!out) return SOLATTN_EINVAL;
-  return layout(mode, dtype, B, H, N, d, block_q, block_k, out);
+  return layout(mode, dtype, B, H, N, d, block_q, block_k, out, N);
 }
 
 size_t solattn_workspace_bytes(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k) {
   solattn_ws_layout L;
-  if (layout(mode, dtype, B, H, N, d, block_q, block_k, &L) != SOLATTN_OK) return 0;
+  if (layout(mode, dtype, B, H, N, d, block_q, block_k, &L, N) != SOLATTN_OK) return 0;
+  return L.total;
+}
+
+int solattn_workspace_layout_rows(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k,
+                                  int q_rows, solattn_ws_layout* out) {
+  if (!out) return SOLATTN_EINVAL;
+  return layout(mode, dtype, B, H, N, d, block_q, block_k, out, q_rows);
+}
+
+size_t solattn_workspace_bytes_rows(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k,
+                                    int q_rows) {
+  solattn_ws_layout L;
+  if (layout(mode, dtype, B, H, N, d, block_q, block_k, &L, q_rows) != SOLATTN_OK) return 0;
   return L.total;
 }
 

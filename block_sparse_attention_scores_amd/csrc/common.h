@@ -16,7 +16,8 @@ struct Tensor {
 struct Problem {
   int B, H, N, d;
   int bq, bk;            // query / key block sizes
-  int Mq, M, Mpad;       // query blocks, key blocks, key blocks rounded up to 64
+  int Mq, M, Mpad;       // query blocks (of the computed window), key blocks, key blocks rounded up to 64
+  int q0;                // first query block of the window (global index); workspace rows are local
   int mode;              // 0 sol, 1 sla, 2 static local 3-D neighbourhood
   int dtype;             // 0 bf16, 1 fp32
   float tau;
@@ -25,7 +26,7 @@ struct Problem {
   int sink_blocks;       // key blocks overlapping [0, sink_range)
   int extra;             // extra tokens per query block (0..256)
   int exact_extra;       // select extra tokens exactly from the start (no seeded pass)
-  int dense_q0, dense_q1;  // query blocks [dense_q0, dense_q1) attend every key
+  int dense_q0, dense_q1;  // window-local query blocks [dense_q0, dense_q1) attend every key
   int frames, height, width;  // local 3-D mode: the token grid (frames*height*width == N)
   float scale;           // 1/sqrt(d)
   Tensor q, k, v, o;

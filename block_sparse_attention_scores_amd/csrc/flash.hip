@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
 
   // this wave's 32 query rows: Q^T operand fragments
   const bool wave_on = valid[g];
-  const int q0 = (valid[g] ? qb[g] : qb[0]) * P.bq + 32 * (w % WPQ);
+  const int q0 = ((valid[g] ? qb[g] : qb[0]) + P.q0) * P.bq + 32 * (w % WPQ);
   bf16x8_t qf[D / 16];
   {
     const uint16_t* qr = Qb + (int64_t)(q0 + c32) * P.q.sn + 8 * h32;
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(BQ) void sparse_flash_f32_kernel(Problem P) {
   const float* Kb = static_cast<const float*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)hh * P.k.sh;
   const float* Vb = static_cast<const float*>(P.v.p) + (int64_t)b * P.v.sb + (int64_t)hh * P.v.sh;
   const float* Qb = static_cast<const float*>(P.q.p) + (int64_t)b * P.q.sb + (int64_t)hh * P.q.sh;
-  const int qrow = qi * BQ + tid;
+  const int qrow = (qi + P.q0) * BQ + tid;
 
   float q[D], o[D];
 #pragma unroll

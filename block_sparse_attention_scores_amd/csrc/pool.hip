@@ -70,8 +70,9 @@ __global__ __launch_bounds__(256) void block_pool_kernel(Problem P) {
 
   const Tensor X = is_q ? P.q : (which == 1 ? P.k : P.v);
   const int b = bh / P.H, h = bh % P.H;
+  const int gblk = is_q ? blk + P.q0 : blk;        // query blocks are counted from the window start
   const T* base = static_cast<const T*>(X.p) + (int64_t)b * X.sb + (int64_t)h * X.sh +
-                  (int64_t)blk * bs * X.sn;
+                  (int64_t)gblk * bs * X.sn;
   const int c = tid % CPR, r0 = tid / CPR;
   const bool write_vt = bf_copies && which == 2;     // bs == 64 for key blocks
 

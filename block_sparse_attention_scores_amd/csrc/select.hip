@@ -91,8 +91,9 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
   }
 
   // forced blocks: the sinks and every key block overlapping this query block's tokens
-  const int diag_lo = (i * P.bq) / P.bk;
-  const int diag_hi = min(M - 1, ((i + 1) * P.bq - 1) / P.bk);
+  const int gi = i + P.q0;                       // global query block (rows are window-local)
+  const int diag_lo = (gi * P.bq) / P.bk;
+  const int diag_hi = min(M - 1, ((gi + 1) * P.bq - 1) / P.bk);
   auto forced = [&](int j) { return j < P.sink_blocks || (j >= diag_lo && j <= diag_hi); };
 
   float theta = 0.f;          // sol threshold
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
     __syncthreads();
     if (tid < P.bq) {
       const int hw = P.height * P.width;
-      const int p = i * P.bq + tid;
+      const int p = gi * P.bq + tid;
       const int t = p / hw, r = p - t * hw;
       const int y = r / P.width, x = r - y * P.width;
       auto mark = [&](int tok) {

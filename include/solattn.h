@@ -75,6 +75,13 @@ typedef struct solattn_opts {
   void*  stream;                  /* hipStream_t; NULL = null stream                       */
   unsigned flags;                 /* SOLATTN_FLAG_* bits; 0 = defaults                       */
   int64_t* stats;                 /* device int64[SOLATTN_NSTATS] for per-call counters, or NULL */
+  /* Query-row window: only rows [q_row_begin, q_row_end) are computed (both multiples of
+   * block_q); the other rows of out are left untouched.  Keys are always all N rows.  Both 0
+   * means every row.  The workspace then covers the window only (see the _rows layout
+   * calls), which is how a caller splits a long sequence into row chunks that fit in memory.
+   * Dense rows are given in whole-sequence coordinates and intersected with the window; the
+   * intermediate buffers (qbar, scores, lists, ...) hold the window's query blocks from 0. */
+  int q_row_begin, q_row_end;
 } solattn_opts;
 
 /*
@@ -228,6 +235,13 @@ int solattn_workspace_layout(int mode, int dtype, int B, int H, int N, int d,
 /* Total workspace bytes for a call of this shape (0 if the shape is invalid). */
 size_t solattn_workspace_bytes(int mode, int dtype, int B, int H, int N, int d,
                                int block_q, int block_k);
+
+/* The same two calls for a query-row window of q_rows rows (opts->q_row_begin/end);
+ * q_rows = N gives the whole-sequence layout.  q_rows in [1, N]. */
+int solattn_workspace_layout_rows(int mode, int dtype, int B, int H, int N, int d,
+                                  int block_q, int block_k, int q_rows, solattn_ws_layout* layout);
+size_t solattn_workspace_bytes_rows(int mode, int dtype, int B, int H, int N, int d,
+                                    int block_q, int block_k, int q_rows);
 
 /* Static text for a status code. */
 const char* solattn_status_string(int status);

@@ -124,6 +124,25 @@ def test_stats_and_flag_validation():
     assert check(opts=sa.make_opts(flags=sa.FLAG_EXACT_EXTRA | sa.FLAG_CHECK_FINITE, stats=1 << 33)) == sa.OK
 
 
+def test_query_row_window_validation_and_layout():
+    assert check(opts=sa.make_opts(q_rows=(1024, 2048))) == sa.OK
+    assert check(opts=sa.make_opts(q_rows=(0, 4096))) == sa.OK
+    for rows in [(2048, 1024), (-64, 64), (0, 4160), (1024, 1024)]:
+        assert check(opts=sa.make_opts(q_rows=rows)) == sa.EINVAL, rows
+        assert "window" in sa.last_error()
+    assert check(opts=sa.make_opts(q_rows=(32, 1024))) == sa.ENOTSUP
+    assert check(mode=1, bq=128, opts=sa.make_opts(q_rows=(64, 1024))) == sa.ENOTSUP
+    # the window's workspace: query-block arrays shrink with the window, key arrays do not
+    full = sa.workspace_layout(0, sa.BF16, 1, 2, 4096, 64, 64, 64)
+    part = sa.workspace_layout(0, sa.BF16, 1, 2, 4096, 64, 64, 64, q_rows=1024)
+    assert (full.Mq, part.Mq, full.M, part.M) == (64, 16, 64, 64)
+    assert part.total < full.total
+    assert part.kbar - part.qbar == 2 * 16 * 64 * 4
+    assert sa.workspace_bytes(0, sa.BF16, 1, 2, 4096, 64, 64, 64, 4096) == full.total
+    assert sa.workspace_bytes(0, sa.BF16, 1, 2, 4096, 64, 64, 64, 0) == 0
+    assert sa.workspace_bytes(0, sa.BF16, 1, 2, 4096, 64, 64, 64, 4097) == 0
+
+
 def test_page_parameter_ranges_are_accepted():
     g = json.load(open(GOLDEN))
     assert check(extra=g["extra_tokens_range"]["max"]) == sa.OK
