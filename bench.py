@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 matrix peak
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 matrix peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
@@ -76,6 +77,8 @@ def parse():
     ap.add_argument("--heads", type=int, default=None, help="override the head count")
     ap.add_argument("--mode", choices=("sol", "sla", "local3d"), default=None,
                     help="override the selection mode")
+    ap.add_argument("--qk-fp8", action="store_true",
+                    help="the fp8-QK flavour (E4M3 score products, bf16 softmax and P V)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
@@ -175,6 +178,10 @@ def main():
     if ov:
         tag = "".join(f"-{k}{v}" for k, v in sorted(ov.items()))
         w = workload(a.config, name=w.name + tag, **ov)
+    if a.qk_fp8:
+        if w.dtype != "bf16":
+            raise SystemExit("--qk-fp8 needs a bf16 workload")
+        w = workload(a.config, name=w.name + "-fp8qk", **ov)
     dev = torch.device("cuda:0")
     log(f"[bench] generating {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}")
     t0 = time.perf_counter()
@@ -187,23 +194,21 @@ def main():
         q, k, v = (torch.from_numpy(t).to(dev) for t in (x.q, x.k, x.v))
     mode = {"sol": sa.MODE_SOL, "sla": sa.MODE_SLA, "local3d": sa.MODE_LOCAL3D}[w.mode]
     out = torch.empty_like(q)
-    ws = sa.alloc_workspace(mode, q, w.block_q, w.block_k)
+    ws = sa.alloc_workspace(mode, q, w.block_q, w.block_k, qk_fp8=a.qk_fp8)
+
+    def call(**extra):
+        common = dict(block_q=w.block_q, block_k=w.block_k, sink_range=w.sink_range,
+                      extra_tokens=w.extra_tokens, dense_rows=w.dense_rows, out=out,
+                      workspace=ws, qk_fp8=a.qk_fp8, **extra)
+        if w.mode == "sol":
+            sa.sol_attn(q, k, v, tau=w.tau, **common)
+        elif w.mode == "local3d":
+            sa.local3d_attn(q, k, v, grid=(w.T, w.Hh, w.Ww), **common)
+        else:
+            sa.sla_attn(q, k, v, keep_percent=w.keep_percent, **common)
 
     def step():
-        if w.mode == "sol":
-            sa.sol_attn(q, k, v, tau=w.tau, block_q=w.block_q, block_k=w.block_k,
-                        sink_range=w.sink_range, extra_tokens=w.extra_tokens,
-                        dense_rows=w.dense_rows, out=out, workspace=ws)
-        elif w.mode == "local3d":
-            sa.local3d_attn(q, k, v, grid=(w.T, w.Hh, w.Ww), block_q=w.block_q,
-                            block_k=w.block_k, sink_range=w.sink_range,
-                            extra_tokens=w.extra_tokens, dense_rows=w.dense_rows, out=out,
-                            workspace=ws)
-        else:
-            sa.sla_attn(q, k, v, keep_percent=w.keep_percent, block_q=w.block_q,
-                        block_k=w.block_k, sink_range=w.sink_range,
-                        extra_tokens=w.extra_tokens, dense_rows=w.dense_rows, out=out,
-                        workspace=ws)
+        call()
 
     for _ in range(a.warmup):
         step()
@@ -241,23 +246,12 @@ def main():
 
     # one more (untimed) call with the library's per-call counters
     stats_t = torch.zeros(sa.NSTATS, dtype=torch.int64, device=dev)
-    if w.mode == "sol":
-        sa.sol_attn(q, k, v, tau=w.tau, block_q=w.block_q, block_k=w.block_k,
-                    sink_range=w.sink_range, extra_tokens=w.extra_tokens, dense_rows=w.dense_rows,
-                    out=out, workspace=ws, stats=stats_t, flags=sa.FLAG_CHECK_FINITE)
-    elif w.mode == "local3d":
-        sa.local3d_attn(q, k, v, grid=(w.T, w.Hh, w.Ww), block_q=w.block_q, block_k=w.block_k,
-                        sink_range=w.sink_range, extra_tokens=w.extra_tokens,
-                        dense_rows=w.dense_rows, out=out, workspace=ws, stats=stats_t,
-                        flags=sa.FLAG_CHECK_FINITE)
-    else:
-        sa.sla_attn(q, k, v, keep_percent=w.keep_percent, block_q=w.block_q, block_k=w.block_k,
-                    sink_range=w.sink_range, extra_tokens=w.extra_tokens, dense_rows=w.dense_rows,
-                    out=out, workspace=ws, stats=stats_t, flags=sa.FLAG_CHECK_FINITE)
+    call(stats=stats_t, flags=sa.FLAG_CHECK_FINITE)
     torch.cuda.synchronize()
     call_stats = dict(zip(sa.STAT_NAMES, (int(x_) for x_ in stats_t.cpu().tolist())))
 
-    views = sa.selection_views(ws, mode, sa.BF16 if w.dtype == "bf16" else sa.FP32, w.B, w.H, w.N,
+    dcode = sa.FP32 if w.dtype != "bf16" else (sa.BF16_FP8QK if a.qk_fp8 else sa.BF16)
+    views = sa.selection_views(ws, mode, dcode, w.B, w.H, w.N,
                                w.d, w.block_q, w.block_k)
     sel = {k_: v_.cpu().numpy() for k_, v_ in views.items()}
     exact_pairs, cent_terms, kept_frac = selection_stats(sel, w, w.B, w.H)
@@ -272,8 +266,11 @@ def main():
             kern[name] = dict(avg_ms=ms / n, launches=n)
     t_flash = kern["sparse_flash_fwd"]["avg_ms"] * 1e-3
     ach = f_exact / t_flash / 1e12
-    roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic(w.name),
+    # the fp8-QK flavour runs half of the exact work (Q K^T) at the fp8 peak and half (P V) at
+    # the bf16 peak: its ceiling is the work-weighted harmonic mix of the two
+    peak = PEAK_BF16_TFLOPS if not a.qk_fp8 else 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+    roof = dict(bound="mfma", achieved=round(ach, 2), peak=round(peak, 1), unit="TFLOP/s",
+                frac=round(ach / peak, 4), traffic=measured_traffic(w.name),
                 kernel="sparse_flash_fwd", algorithmic_flop=f_exact)
     # the other kernels against their own rooflines
     # pool: read Q, K, V; write the fp32 means, and for bf16 the transposed V tiles and the
@@ -302,7 +299,7 @@ def main():
         kern["extra_select"].update(bound="mfma", achieved_TFLOPs=round(fl / t / 1e12, 2),
                                     frac=round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4))
     kern["sparse_flash_fwd"].update(bound="mfma", achieved_TFLOPs=round(ach, 2),
-                                    frac=round(ach / PEAK_BF16_TFLOPS, 4))
+                                    frac=round(ach / peak, 4))
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -325,7 +322,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "fp8-e4m3 QK + bf16 PV" if a.qk_fp8 else w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "mode": w.mode, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "block_q": w.block_q, "block_k": w.block_k, "tau": w.tau,

@@ -4,7 +4,7 @@ The compute path is libsolattn, hand-written HIP for gfx950 behind a C ABI
 (include/solattn.h); this package is its thin Python binding.
 """
 from ._lib import (  # noqa: F401
-    BF16, FP32, MODE_SOL, MODE_SLA, MODE_LOCAL3D, MAX_EXTRA, OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP,
+    BF16, FP32, BF16_FP8QK, MODE_SOL, MODE_SLA, MODE_LOCAL3D, MAX_EXTRA, OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP,
     FLAG_EXACT_EXTRA, FLAG_CHECK_FINITE, NSTATS, STAT_NAMES,
     SolattnError, Opts, WsLayout, lib, sol_attn, sla_attn, local3d_attn, workspace_layout, workspace_bytes,
     alloc_workspace, selection_views, status_string, last_error, kernel_names, timing_enable,

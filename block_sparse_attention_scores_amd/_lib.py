@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libsolattn.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "solattn.h")
 
 OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
-BF16, FP32 = 0, 1
+BF16, FP32, BF16_FP8QK = 0, 1, 2
 MODE_SOL, MODE_SLA, MODE_LOCAL3D = 0, 1, 2
 MAX_EXTRA = 256
 NKERNELS = 5
@@ -58,7 +58,8 @@ class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "total", "qbar", "kbar", "vbar", "scores", "kept_cnt", "kept_idx", "kept_bm", "mult", "cbias", "extra_cnt",
         "extra_idx", "extra_buf", "extra_part", "extra_flag", "kbar_bf", "vbar_t", "v_t")] + [
-        ("Mq", ctypes.c_int), ("M", ctypes.c_int), ("Mpad", ctypes.c_int)]
+        ("Mq", ctypes.c_int), ("M", ctypes.c_int), ("Mpad", ctypes.c_int),
+        ("k8", ctypes.c_size_t), ("kb8", ctypes.c_size_t)]
 
 
 _lib = None
@@ -176,8 +177,12 @@ def _torch():
     return torch
 
 
-def _dtype_code(t) -> int:
+def _dtype_code(t, qk_fp8=False) -> int:
     torch = _torch()
+    if qk_fp8:
+        if t.dtype != torch.bfloat16:
+            raise TypeError("the fp8-QK flavour takes bfloat16 tensors")
+        return BF16_FP8QK
     if t.dtype == torch.bfloat16:
         return BF16
     if t.dtype == torch.float32:
@@ -196,17 +201,18 @@ def _check_tensor(name, t, shape, dtype):
         raise ValueError(f"{name}: the d axis must be contiguous")
 
 
-def alloc_workspace(mode, q, block_q, block_k, q_rows=None):
+def alloc_workspace(mode, q, block_q, block_k, q_rows=None, qk_fp8=False):
     """A workspace for a call on q's shape (or on the query-row window q_rows = (begin, end))."""
     torch = _torch()
     B, H, N, d = q.shape
     rows = None if q_rows is None else q_rows[1] - q_rows[0]
-    nbytes = workspace_bytes(mode, _dtype_code(q), B, H, N, d, block_q, block_k, rows)
+    nbytes = workspace_bytes(mode, _dtype_code(q, qk_fp8), B, H, N, d, block_q, block_k, rows)
     return torch.empty(nbytes, dtype=torch.uint8, device=q.device)
 
 
 def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, extra_tokens,
-          dense_rows, out, workspace, stream, flags=0, grid=None, stats=None, q_rows=None):
+          dense_rows, out, workspace, stream, flags=0, grid=None, stats=None, q_rows=None,
+          qk_fp8=False):
     torch = _torch()
     B, H, N, d = q.shape
     for n, t in (("k", k), ("v", v)):
@@ -216,7 +222,7 @@ def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, ext
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     _check_tensor("out", out, q.shape, q.dtype)
     if workspace is None:
-        workspace = alloc_workspace(mode, q, block_q, block_k, q_rows)
+        workspace = alloc_workspace(mode, q, block_q, block_k, q_rows, qk_fp8)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     strides = [tuple(t.stride()[:3]) for t in (q, k, v, out)]
@@ -224,7 +230,7 @@ def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, ext
         if not stats.is_cuda or stats.dtype != torch.int64 or stats.numel() < NSTATS \
                 or not stats.is_contiguous():
             raise ValueError(f"stats must be a contiguous int64 GPU tensor of >= {NSTATS} elements")
-    opts = make_opts(_dtype_code(q), strides, dense_rows, workspace.data_ptr(),
+    opts = make_opts(_dtype_code(q, qk_fp8), strides, dense_rows, workspace.data_ptr(),
                      workspace.numel() * workspace.element_size(), stream, flags,
                      stats.data_ptr() if stats is not None else 0, q_rows)
     L = lib()
@@ -247,30 +253,32 @@ def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, ext
 
 def sol_attn(q, k, v, *, tau=1.3, block_q=64, block_k=64, sink_range=0, extra_tokens=0,
              dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False,
-             flags=0, stats=None, q_rows=None):
+             flags=0, stats=None, q_rows=None, qk_fp8=False):
     """sol-attn forward on [B, H, N, d] GPU tensors (bfloat16 or float32); see include/solattn.h.
     stats: optional int64 GPU tensor of NSTATS elements for the per-call counters; q_rows:
-    optional (begin, end) query-row window (only those rows of out are written)."""
+    optional (begin, end) query-row window (only those rows of out are written); qk_fp8: the
+    fp8-QK flavour (SOLATTN_BF16_FP8QK, bfloat16 tensors)."""
     o, ws = _call(MODE_SOL, q, k, v, tau=tau, keep_percent=0.0, block_q=block_q, block_k=block_k,
                   sink_range=sink_range, extra_tokens=extra_tokens, dense_rows=dense_rows, out=out,
-                  workspace=workspace, stream=stream, flags=flags, stats=stats, q_rows=q_rows)
+                  workspace=workspace, stream=stream, flags=flags, stats=stats, q_rows=q_rows,
+                  qk_fp8=qk_fp8)
     return (o, ws) if return_workspace else o
 
 
 def sla_attn(q, k, v, *, keep_percent=10.0, block_q=128, block_k=64, sink_range=0, extra_tokens=0,
              dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False,
-             flags=0, stats=None, q_rows=None):
+             flags=0, stats=None, q_rows=None, qk_fp8=False):
     """sla forward on [B, H, N, d] GPU tensors (bfloat16 or float32); see include/solattn.h."""
     o, ws = _call(MODE_SLA, q, k, v, tau=0.0, keep_percent=keep_percent, block_q=block_q,
                   block_k=block_k, sink_range=sink_range, extra_tokens=extra_tokens,
                   dense_rows=dense_rows, out=out, workspace=workspace, stream=stream, flags=flags,
-                  stats=stats, q_rows=q_rows)
+                  stats=stats, q_rows=q_rows, qk_fp8=qk_fp8)
     return (o, ws) if return_workspace else o
 
 
 def local3d_attn(q, k, v, *, grid, block_q=64, block_k=64, sink_range=0, extra_tokens=0,
                  dense_rows=(0, 0), out=None, workspace=None, stream=None, return_workspace=False,
-                 flags=0, stats=None, q_rows=None):
+                 flags=0, stats=None, q_rows=None, qk_fp8=False):
     """Static local 3-D neighbourhood forward on [B, H, N, d] GPU tensors; grid = (frames,
     height, width) with frames*height*width == N; see include/solattn.h."""
     if len(grid) != 3:
@@ -278,7 +286,7 @@ def local3d_attn(q, k, v, *, grid, block_q=64, block_k=64, sink_range=0, extra_t
     o, ws = _call(MODE_LOCAL3D, q, k, v, tau=0.0, keep_percent=100.0, block_q=block_q,
                   block_k=block_k, sink_range=sink_range, extra_tokens=extra_tokens,
                   dense_rows=dense_rows, out=out, workspace=workspace, stream=stream, flags=flags,
-                  grid=grid, stats=stats, q_rows=q_rows)
+                  grid=grid, stats=stats, q_rows=q_rows, qk_fp8=qk_fp8)
     return (o, ws) if return_workspace else o
 
 

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsolattn.so")
-SOURCES = ["api.cpp", "pool.hip", "score.hip", "select.hip", "extra.hip", "flash.hip", "stats.hip"]
+SOURCES = ["api.cpp", "pool.hip", "score.hip", "select.hip", "extra.hip", "flash.hip", "stats.hip", "quant.hip"]
 ARCH = os.environ.get("SOLATTN_ARCH", "gfx950")
 
 COMMON = [

@@ -69,7 +69,7 @@ def chunked_attention(method: str, q, k, v, *, chunk_rows: int, block_q: int = 6
                       block_k: int = 64, out=None, alloc=None, **params):
     """Run ``method`` ("sol", "sla" or "local3d") over [B, H, N, d] GPU tensors in chunks of
     ``chunk_rows`` query rows.  ``params`` go to the library call (tau, keep_percent, grid,
-    sink_range, extra_tokens, dense_rows, flags, stream).  ``alloc(nbytes)`` returns a uint8
+    sink_range, extra_tokens, dense_rows, flags, stream, qk_fp8).  ``alloc(nbytes)`` returns a uint8
     workspace tensor (default: torch.empty on q's device); an out-of-memory error from it or
     from the call halves the chunk.  Returns (out, ChunkReport)."""
     import torch
@@ -88,8 +88,8 @@ def chunked_attention(method: str, q, k, v, *, chunk_rows: int, block_q: int = 6
 
     def attempt(begin, end):
         try:
-            nbytes = L.workspace_bytes(modes[method], L._dtype_code(q), B, H, N, d, block_q,
-                                       block_k, end - begin)
+            nbytes = L.workspace_bytes(modes[method], L._dtype_code(q, params.get("qk_fp8", False)),
+                                       B, H, N, d, block_q, block_k, end - begin)
             ws = alloc(nbytes)
             calls[method](q, k, v, block_q=block_q, block_k=block_k, out=out, workspace=ws,
                           q_rows=(begin, end), **params)

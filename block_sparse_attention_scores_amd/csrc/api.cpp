@@ -63,7 +63,8 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   if (opts && opts->struct_size != (int)sizeof(solattn_opts))
     return fail(SOLATTN_EINVAL, "opts->struct_size %d != %d", opts->struct_size, (int)sizeof(solattn_opts));
   const int dtype = opts ? opts->dtype : SOLATTN_BF16;
-  if (dtype != SOLATTN_BF16 && dtype != SOLATTN_FP32) return fail(SOLATTN_EINVAL, "dtype %d", dtype);
+  if (dtype != SOLATTN_BF16 && dtype != SOLATTN_FP32 && dtype != SOLATTN_BF16_FP8QK)
+    return fail(SOLATTN_EINVAL, "dtype %d", dtype);
   if (!q || !k || !v || !out) return fail(SOLATTN_EINVAL, "null tensor pointer");
   if (B < 1 || H < 1 || N < 1 || d < 1) return fail(SOLATTN_EINVAL, "sizes B=%d H=%d N=%d d=%d", B, H, N, d);
   if (block_q < 1 || block_k < 1) return fail(SOLATTN_EINVAL, "block sizes %d %d", block_q, block_k);
@@ -102,7 +103,7 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   const Strides& so = st[3];
   if (so.sn < d || (H > 1 && so.sh < (int64_t)N * so.sn) || (B > 1 && so.sb < (int64_t)H * so.sh))
     return fail(SOLATTN_EINVAL, "out strides make rows overlap");
-  const size_t es = dtype == SOLATTN_BF16 ? 2 : 4;
+  const size_t es = dtype == SOLATTN_FP32 ? 4 : 2;
   uintptr_t olo, ohi;
   extent(out, so, B, H, N, d, es, &olo, &ohi);
   const void* ins[3] = {q, k, v};
@@ -119,7 +120,7 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   if (d0 % block_q || d1 % block_q) return fail(SOLATTN_ENOTSUP, "dense rows not block_q aligned");
   if (r0 % block_q || r1 % block_q) return fail(SOLATTN_ENOTSUP, "query-row window not block_q aligned");
   if ((int64_t)B * H > 65535) return fail(SOLATTN_ENOTSUP, "B*H=%lld too large", (long long)B * H);
-  if (dtype == SOLATTN_BF16 && N / block_k > solattn::MAX_BLOCKS_BF16)
+  if (dtype != SOLATTN_FP32 && N / block_k > solattn::MAX_BLOCKS_BF16)
     return fail(SOLATTN_ENOTSUP, "bf16: more than %d key blocks", solattn::MAX_BLOCKS_BF16);
   if (mode == SOLATTN_MODE_LOCAL3D && N / block_k > solattn::MAX_BLOCKS_LOCAL3D)
     return fail(SOLATTN_ENOTSUP, "local 3-D: more than %d key blocks", solattn::MAX_BLOCKS_LOCAL3D);
@@ -139,7 +140,7 @@ int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int blo
            int q_rows) {
   (void)mode;
   if (B < 1 || H < 1 || N < 1 || d < 1 || block_q < 1 || block_k < 1 || q_rows < 1 || q_rows > N ||
-      (dtype != SOLATTN_BF16 && dtype != SOLATTN_FP32))
+      (dtype != SOLATTN_BF16 && dtype != SOLATTN_FP32 && dtype != SOLATTN_BF16_FP8QK))
     return SOLATTN_EINVAL;
   std::memset(L, 0, sizeof *L);
   const size_t BH = (size_t)B * H;
@@ -166,10 +167,15 @@ int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int blo
   L->extra_buf = take(BH * Mq * S * 4 * solattn::EXTRA_CAP * 8);
   L->extra_part = take(BH * Mq * S * 4 * 4);
   L->extra_flag = take(BH * Mq * 4);
-  if (dtype == SOLATTN_BF16) {
+  if (dtype != SOLATTN_FP32) {
     L->kbar_bf = take(BH * Mpad * d * 2);
     L->vbar_t = take(BH * Mpad * d * 2);
     L->v_t = take(BH * (size_t)M * d * 64 * 2);
+  }
+  if (dtype == SOLATTN_BF16_FP8QK) {
+    const size_t tb = (size_t)64 * d + 64;
+    L->k8 = take(BH * (size_t)M * tb);
+    L->kb8 = take(BH * (size_t)(Mpad / 64) * tb);
   }
   L->total = off;
   L->Mq = Mq;
@@ -258,7 +264,9 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   P.B = B; P.H = H; P.N = N; P.d = d;
   P.bq = block_q; P.bk = block_k;
   P.Mq = L.Mq; P.M = L.M; P.Mpad = L.Mpad;
-  P.mode = mode; P.dtype = dtype;
+  P.mode = mode;
+  P.dtype = dtype == SOLATTN_FP32 ? 1 : 0;      // the element type of the tensors
+  P.fp8qk = dtype == SOLATTN_BF16_FP8QK ? 1 : 0;
   P.tau = tau;
   P.keep_all = (mode == SOLATTN_MODE_SOL && std::isinf(tau) && tau < 0) ? 1 : 0;
   if (mode == SOLATTN_MODE_SLA) {
@@ -295,10 +303,14 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   P.extra_part = reinterpret_cast<int*>(ws + L.extra_part);
   P.extra_flag = reinterpret_cast<int*>(ws + L.extra_flag);
   P.extra_slices = solattn::extra_slice_count(B, H, L.Mq);
-  if (dtype == SOLATTN_BF16) {
+  if (dtype != SOLATTN_FP32) {
     P.kbar_bf = reinterpret_cast<uint16_t*>(ws + L.kbar_bf);
     P.vbar_t = reinterpret_cast<uint16_t*>(ws + L.vbar_t);
     P.v_t = reinterpret_cast<uint16_t*>(ws + L.v_t);
+  }
+  if (P.fp8qk) {
+    P.k8 = reinterpret_cast<uint8_t*>(ws + L.k8);
+    P.kb8 = reinterpret_cast<uint8_t*>(ws + L.kb8);
   }
 
   if (opts && opts->stats && L.extra_part - L.extra_buf < solattn::stats_scratch_bytes())
@@ -334,6 +346,8 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   auto launch_all = [&]() -> const char* {
     mark(0);
     if ((err = solattn::launch_block_pool(P, stream)) != hipSuccess) return "block_pool";
+    // the fp8 key tiles need the pooled keys; their time is counted with the pooling
+    if (P.fp8qk && (err = solattn::launch_quantize_k(P, stream)) != hipSuccess) return "quantize_k";
     tc.ran[0] = true;
     mark(1);
     if (mode != SOLATTN_MODE_LOCAL3D) {

@@ -19,7 +19,8 @@ struct Problem {
   int Mq, M, Mpad;       // query blocks (of the computed window), key blocks, key blocks rounded up to 64
   int q0;                // first query block of the window (global index); workspace rows are local
   int mode;              // 0 sol, 1 sla, 2 static local 3-D neighbourhood
-  int dtype;             // 0 bf16, 1 fp32
+  int dtype;             // element type of q, k, v, out: 0 bf16, 1 fp32
+  int fp8qk;             // bf16 tensors, QK^T products on E4M3 operands (the fp8-QK flavour)
   float tau;
   int keep_all;          // tau == -inf: every block kept
   int k_sla;             // sla: ceil(keep_percent * M / 100)
@@ -46,6 +47,8 @@ struct Problem {
   int* extra_part;       // per query block, token slice and wave: entries left after the final cut
   int* extra_flag;       // per query block: 1 when the seeded threshold left too few candidates
   int extra_slices;      // token slices of the extra-token selection
+  uint8_t* k8;           // fp8-QK: E4M3 key tiles [B*H, M] of 64*d bytes + 64 scale codes
+  uint8_t* kb8;          // fp8-QK: E4M3 pooled-key tiles [B*H, Mpad/64], same layout
   uint16_t* kbar_bf;
   uint16_t* vbar_t;
   uint16_t* v_t;
@@ -97,6 +100,26 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // instruction (given the 32x32 accumulator layout of the score tile) sit next to each other.
 __host__ __device__ __forceinline__ int vt_pos(int kk) {
   return (kk & ~0xC) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+}
+
+// E4M3 scaling (the fp8-QK flavour): e = the smallest integer with amax <= 448 * 2^e
+// (amax > 0; 0 for amax = 0), clamped to the E8M0 code range [-127, 127].
+__device__ __forceinline__ int e4m3_scale_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int k;
+  (void)frexpf(amax, &k);                     // amax in [2^(k-1), 2^k)
+  const int e = (ldexpf(amax, 9 - k) <= 448.f) ? k - 9 : k - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Eight values, already scaled into [-448, 448], as eight E4M3 bytes (nearest, ties to even),
+// little-endian in a uint2.
+__device__ __forceinline__ uint2 pack8_e4m3(const float* x) {
+  uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0u, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+  uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0u, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
+  return make_uint2(lo, hi);
 }
 
 }  // namespace solattn

@@ -25,6 +25,7 @@ namespace solattn {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -53,15 +54,20 @@ __device__ __forceinline__ int kswz(int r, int c) {
   else return c ^ ((r >> 1) & 7);                     // 128-byte rows
 }
 __device__ __forceinline__ int vswz(int r, int c) { return c ^ ((r >> 1) & 7); }   // 128-byte rows
-
-// Double-buffered LDS tiles.  K: 64 keys x D (chunk-swizzled rows).  V: transposed, D rows of 64
-// keys (chunk-swizzled).  Bias: per query block of the pair, per key (centroid and extra tiles).
+// E4M3 key rows (fp8-QK): D bytes, D/16 chunks
 template <int D>
+__device__ __forceinline__ int kswz8(int r, int c) { return c ^ ((r >> 1) & (D / 16 - 1)); }
+
+// Double-buffered LDS tiles.  K: 64 keys x D (chunk-swizzled rows; bf16, or E4M3 bytes plus the
+// rows' scale codes for the fp8-QK flavour).  V: transposed, D rows of 64 keys (chunk-swizzled).
+// Bias: per query block of the pair, per key (centroid and extra tiles).
+template <int D, bool QK8>
 struct FlashSmem {
-  __attribute__((aligned(16))) uint16_t k[2][64 * D];
+  __attribute__((aligned(16))) uint8_t k[2][QK8 ? 64 * D : 128 * D];
   __attribute__((aligned(16))) uint16_t v[2][64 * D];
   __attribute__((aligned(16))) float bias[2][2][64];
   __attribute__((aligned(16))) float zero[64];   // the bias of plain key tiles
+  __attribute__((aligned(16))) uint8_t ke[2][QK8 ? 64 : 16];   // E4M3 scale codes of the K rows
 };
 
 struct TileDesc {
@@ -136,13 +142,17 @@ __device__ __forceinline__ bool flash_unit(const Problem& P, int G, int gid, int
 }
 
 // WPQ waves per query block (block_q / 32), G query blocks per workgroup; WPQ * G = 4.
-template <int D, int WPQ, int G>
-__global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
-  __shared__ FlashSmem<D> sm;
-  constexpr int KCH = D / 8;                 // 16-byte chunks per K row
-  constexpr int SLOTS = 64 * D / 8;          // 16-byte slots per tile matrix
+// QK8: the fp8-QK flavour (E4M3 key tiles and query fragments, scaled products for S).
+template <int D, int WPQ, int G, bool QK8>
+__device__ __forceinline__ void sparse_flash_body(const Problem& P) {
+  __shared__ FlashSmem<D, QK8> sm;
+  constexpr int KCH = D / 8;                 // 16-byte chunks per bf16 K row (and per V^T row pair)
+  constexpr int SLOTS = 64 * D / 8;          // 16-byte slots per bf16 tile matrix
   constexpr int PER_THREAD = SLOTS / 256;
   constexpr int TILE_BYTES = 64 * D * 2;
+  constexpr int KCH8 = D / 16;               // 16-byte chunks per E4M3 K row
+  constexpr int PER_THREAD8 = 64 * D / 16 / 256;
+  constexpr uint32_t TB8 = 64 * D + 64;      // E4M3 tile: rows, then the rows' scale codes
   int bh, pair;
   if (!flash_unit(P, G, blockIdx.x, &bh, &pair)) return;
   // the wave index is uniform: read it into a scalar so that every per-wave decision (which
@@ -185,11 +195,46 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
   // this wave's 32 query rows: Q^T operand fragments
   const bool wave_on = valid[g];
   const int q0 = ((valid[g] ? qb[g] : qb[0]) + P.q0) * P.bq + 32 * (w % WPQ);
-  bf16x8_t qf[D / 16];
-  {
+  bf16x8_t qf[QK8 ? 1 : D / 16];
+  i32x8_t qf8[QK8 ? D / 64 : 1];
+  int qcode = 127;
+  if constexpr (!QK8) {
     const uint16_t* qr = Qb + (int64_t)(q0 + c32) * P.q.sn + 8 * h32;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * ks);
+  } else {
+    // E4M3 query row, scaled by its power of two: lane (h32, row) holds d = 64ks + 32h32 .. +31
+    const uint16_t* qr = Qb + (int64_t)(q0 + c32) * P.q.sn + 32 * h32;
+    float x[D / 64][32];
+    float amax = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(qr + 64 * ks + 8 * c);
+        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[ks][8 * c + 2 * e] = __uint_as_float(wd[e] << 16);
+          x[ks][8 * c + 2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
+          amax = fmaxf(amax, fmaxf(fabsf(x[ks][8 * c + 2 * e]), fabsf(x[ks][8 * c + 2 * e + 1])));
+        }
+      }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+    amax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // the whole row
+    const int ex = e4m3_scale_exp(amax);
+    qcode = ex + 127;
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[ks][e] = ldexpf(x[ks][e], -ex);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint2 p = pack8_e4m3(&x[ks][8 * c]);
+        qf8[ks][2 * c] = static_cast<int>(p.x);
+        qf8[ks][2 * c + 1] = static_cast<int>(p.y);
+      }
+    }
   }
 
   // per-lane byte offsets of the tile loads (slot s of this lane in instruction u):
@@ -197,13 +242,24 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
   // transposed V row vr = s / 8, chunk vc = s % 8, stored at vswz(vr, vc).
   const uint32_t ksn_b = static_cast<uint32_t>(P.k.sn) * 2u;
   const uint32_t vsn_b = static_cast<uint32_t>(P.v.sn) * 2u;
-  uint32_t krow[PER_THREAD], kcol[PER_THREAD], voff[PER_THREAD];
+  constexpr int PK = QK8 ? PER_THREAD8 : PER_THREAD;
+  uint32_t krow[PK], kcol[PK], voff[PER_THREAD];
+#pragma unroll
+  for (int u = 0; u < PK; ++u) {
+    const int s = (u * 4 + w) * 64 + l;
+    if constexpr (QK8) {
+      const int r = s / KCH8, c = s % KCH8;
+      krow[u] = r;
+      kcol[u] = kswz8<D>(r, c) * 16;
+    } else {
+      const int r = s / KCH, c = s % KCH;
+      krow[u] = r;
+      kcol[u] = kswz<D>(r, c) * 16;
+    }
+  }
 #pragma unroll
   for (int u = 0; u < PER_THREAD; ++u) {
     const int s = (u * 4 + w) * 64 + l;
-    const int r = s / KCH, c = s % KCH;
-    krow[u] = r;
-    kcol[u] = kswz<D>(r, c) * 16;
     const int vr = s / 8, vc = s % 8;
     voff[u] = vr * 128 + vswz(vr, vc) * 16;
   }
@@ -224,12 +280,23 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
       krow_b = D * 2;
       vbase = P.vbar_t + ((size_t)bh * (P.Mpad / 64) + t.idx / 64) * D * 64;
     }
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, 64u * krow_b);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, TILE_BYTES);
+    if constexpr (QK8) {
+      const uint8_t* k8base = t.kind == 0 ? P.k8 + ((size_t)bh * P.M + t.idx) * TB8
+                                          : P.kb8 + ((size_t)bh * (P.Mpad / 64) + t.idx / 64) * TB8;
+      const __amdgpu_buffer_rsrc_t kr = make_rsrc(k8base, TB8);
 #pragma unroll
-    for (int u = 0; u < PER_THREAD; ++u) {
-      buf_to_lds16(kr, krow[u] * krow_b + kcol[u], kd + u * 4096);
-      buf_to_lds16(vr, voff[u], vd + u * 4096);
+      for (int u = 0; u < PER_THREAD8; ++u) buf_to_lds16(kr, krow[u] * D + kcol[u], kd + u * 4096);
+      if (w == 0 && l < 4) buf_to_lds16(kr, 64 * D + 16 * l, sm.ke[bf]);   // the rows' scale codes
+#pragma unroll
+      for (int u = 0; u < PER_THREAD; ++u) buf_to_lds16(vr, voff[u], vd + u * 4096);
+    } else {
+      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, 64u * krow_b);
+#pragma unroll
+      for (int u = 0; u < PER_THREAD; ++u) {
+        buf_to_lds16(kr, krow[u] * krow_b + kcol[u], kd + u * 4096);
+        buf_to_lds16(vr, voff[u], vd + u * 4096);
+      }
     }
     if (t.kind == 2 && w == 0 && l < 32) {
       // the 64 biases of both query blocks (consecutive rows): lanes 0-15 block 0, 16-31 block 1
@@ -309,15 +376,33 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      // S^T (keys 32kt..32kt+31) += K Q^T; K fragments of step ks+1 read during step ks
-      bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt_ + ak + kt * 32 * D * 2);
+      if constexpr (!QK8) {
+        // S^T (keys 32kt..32kt+31) += K Q^T; K fragments of step ks+1 read during step ks
+        bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt_ + ak + kt * 32 * D * 2);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        bf16x8_t n = a;
-        if (ks + 1 < D / 16)
-          n = *reinterpret_cast<const bf16x8_t*>(kt_ + ((ak ^ (32u * (ks + 1))) + kt * 32 * D * 2));
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
-        a = n;
+        for (int ks = 0; ks < D / 16; ++ks) {
+          bf16x8_t n = a;
+          if (ks + 1 < D / 16)
+            n = *reinterpret_cast<const bf16x8_t*>(kt_ + ((ak ^ (32u * (ks + 1))) + kt * 32 * D * 2));
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
+          a = n;
+        }
+      } else {
+        // S^T += (K 2^ek) (Q 2^eq)^T on E4M3 operands: lane (h32, key row) holds
+        // d = 64ks + 32h32 .. +31 of its row, the same d order as the query fragments
+        const int row = 32 * kt + c32;
+        const int kcode = sm.ke[bf][row];
+#pragma unroll
+        for (int ks = 0; ks < D / 64; ++ks) {
+          const int c0 = 4 * ks + 2 * h32;
+          const uint4 lo = *reinterpret_cast<const uint4*>(kt_ + row * D + kswz8<D>(row, c0) * 16);
+          const uint4 hi = *reinterpret_cast<const uint4*>(kt_ + row * D + kswz8<D>(row, c0 + 1) * 16);
+          const i32x8_t a = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
+                             static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
+                             static_cast<int>(hi.z), static_cast<int>(hi.w)};
+          s[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[ks], s[kt], 0, 0, 0, kcode, 0,
+                                                                  qcode);
+        }
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -391,17 +476,33 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
 #pragma unroll 1
     for (int e0 = 0; e0 < cnt; e0 += 64) {
       __syncthreads();
-      uint16_t* kd = sm.k[0];
       uint16_t* vd = sm.v[0];
+      if constexpr (QK8) {
+        // E4M3 key rows (and their scale codes) from the quantised tiles
+#pragma unroll
+        for (int u = 0; u < PER_THREAD8; ++u) {
+          const int sl = (u * 4 + w) * 64 + l;
+          const int r = sl / KCH8, c = sl % KCH8;
+          const int e = e0 + r < cnt ? e0 + r : e0;             // padding rows reuse a real token
+          const uint32_t tok = static_cast<uint32_t>(el[e]);
+          const uint8_t* trow = P.k8 + ((size_t)bh * P.M + tok / 64) * TB8;
+          *reinterpret_cast<uint4*>(sm.k[0] + r * D + kswz8<D>(r, c) * 16) =
+              *reinterpret_cast<const uint4*>(trow + (tok % 64) * D + c * 16);
+          if (c == 0) sm.ke[0][r] = trow[64 * D + tok % 64];
+        }
+      }
 #pragma unroll
       for (int u = 0; u < PER_THREAD; ++u) {
         const int sl = (u * 4 + w) * 64 + l;
         const int r = sl / KCH, c = sl % KCH;
         const int e = e0 + r < cnt ? e0 + r : e0;               // padding rows reuse a real token
         const uint32_t tok = static_cast<uint32_t>(el[e]);
-        const uint4 kv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Kb) +
-                                                         (size_t)tok * ksn_b + c * 16);
-        *reinterpret_cast<uint4*>(kd + r * D + kswz<D>(r, c) * 8) = kv;
+        if constexpr (!QK8) {
+          uint16_t* kd = reinterpret_cast<uint16_t*>(sm.k[0]);
+          const uint4 kv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Kb) +
+                                                           (size_t)tok * ksn_b + c * 16);
+          *reinterpret_cast<uint4*>(kd + r * D + kswz<D>(r, c) * 8) = kv;
+        }
         const uint4 vv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Vb) +
                                                          (size_t)tok * vsn_b + c * 16);
         const uint16_t* vx = reinterpret_cast<const uint16_t*>(&vv);
@@ -438,6 +539,17 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
       for (int e = 0; e < 4; ++e) pk[e] = static_cast<__bf16>(o[dt][4 * gq + e] * inv);
       *reinterpret_cast<bf16x4_t*>(Ob + d0) = pk;
     }
+}
+
+template <int D, int WPQ, int G>
+__global__ __launch_bounds__(256, 2) void sparse_flash_bf16_kernel(Problem P) {
+  sparse_flash_body<D, WPQ, G, false>(P);
+}
+
+// the fp8-QK flavour: E4M3 score products, bf16 softmax and P V
+template <int D, int WPQ, int G>
+__global__ __launch_bounds__(256, 2) void sparse_flash_fp8qk_kernel(Problem P) {
+  sparse_flash_body<D, WPQ, G, true>(P);
 }
 
 // fp32 path: workgroup -> (head, query block), dense query blocks (the heaviest) first.
@@ -568,7 +680,15 @@ hipError_t launch_sparse_flash(const Problem& P, hipStream_t stream) {
     const int units = P.B * P.H * Mp;
     const int per_round = 8 * XCD_RUN;
     dim3 grid((units + per_round - 1) / per_round * per_round);
-    if (P.bq == 64) {
+    if (P.fp8qk) {
+      if (P.bq == 64) {
+        if (P.d == 128) hipLaunchKernelGGL((sparse_flash_fp8qk_kernel<128, 2, 2>), grid, dim3(256), 0, stream, P);
+        else hipLaunchKernelGGL((sparse_flash_fp8qk_kernel<64, 2, 2>), grid, dim3(256), 0, stream, P);
+      } else {
+        if (P.d == 128) hipLaunchKernelGGL((sparse_flash_fp8qk_kernel<128, 4, 1>), grid, dim3(256), 0, stream, P);
+        else hipLaunchKernelGGL((sparse_flash_fp8qk_kernel<64, 4, 1>), grid, dim3(256), 0, stream, P);
+      }
+    } else if (P.bq == 64) {
       if (P.d == 128) hipLaunchKernelGGL((sparse_flash_bf16_kernel<128, 2, 2>), grid, dim3(256), 0, stream, P);
       else hipLaunchKernelGGL((sparse_flash_bf16_kernel<64, 2, 2>), grid, dim3(256), 0, stream, P);
     } else {

@@ -5,6 +5,7 @@
 namespace solattn {
 
 hipError_t launch_block_pool(const Problem& P, hipStream_t stream);
+hipError_t launch_quantize_k(const Problem& P, hipStream_t stream);   // fp8-QK key tiles
 hipError_t launch_block_score(const Problem& P, hipStream_t stream);
 hipError_t launch_block_select(const Problem& P, hipStream_t stream);
 hipError_t launch_extra_select(const Problem& P, hipStream_t stream);

@@ -47,6 +47,15 @@ extern "C" {
 /* Element types of q, k, v and out (all four share one type). */
 #define SOLATTN_BF16 0
 #define SOLATTN_FP32 1
+/*
+ * bf16 tensors with the fp8-QK flavour of the attention step (the pages' reduced-precision
+ * "INT8 QK, FP16 PV" variants, on the FP8 format): the products Q K^T of the exact tokens and of
+ * the centroids run on E4M3 operands, Q scaled per query row, K per token and the pooled keys
+ * per pooled row by powers of two (the smallest 2^e with max|row| <= 448 * 2^e), rounded to
+ * nearest even; the softmax and P V are those of SOLATTN_BF16, and the selection (kept blocks,
+ * extra tokens) is unchanged.  Not value-identical to SOLATTN_BF16.  d in {64, 128}.
+ */
+#define SOLATTN_BF16_FP8QK 2
 
 /* Selection modes. */
 #define SOLATTN_MODE_SOL 0
@@ -217,6 +226,8 @@ int local3d_check_args(const void* q, const void* k, const void* v, void* out,
  *             candidate competing (the result is exact either way)
  *   kbar_bf   bf16 [B*H, Mpad, d], vbar_t bf16 [B*H, Mpad/64, d, 64], v_t bf16
  *             [B*H, M, d, 64]: operand copies for the attention kernel (bf16 only)
+ *   k8, kb8   E4M3 tiles [B*H, M] and [B*H, Mpad/64] of 64 * d bytes (64 rows) followed by
+ *             the 64 rows' scale codes e + 127 (SOLATTN_BF16_FP8QK only)
  * Mq = N/block_q, M = N/block_k, Mpad = M rounded up to a multiple of 64.
  */
 typedef struct solattn_ws_layout {
@@ -226,6 +237,7 @@ typedef struct solattn_ws_layout {
   size_t extra_flag;             /* int32 [B*H, Mq]: 1 = selection redone exactly            */
   size_t kbar_bf, vbar_t, v_t;
   int Mq, M, Mpad;
+  size_t k8, kb8;                /* SOLATTN_BF16_FP8QK only: E4M3 key and pooled-key tiles  */
 } solattn_ws_layout;
 
 /* Fills *layout for a call of this shape.  Returns SOLATTN_OK or SOLATTN_EINVAL. */

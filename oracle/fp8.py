@@ -8,9 +8,9 @@ page: int8_qk / int8_pv) and say they are not value-identical to BF16.  This fla
   * E4M3 values: sign, 4-bit exponent with bias 7, 3-bit mantissa; the zero exponent field
     holds the subnormals (step 2^-9); the largest finite value is 448; rounding is to nearest,
     ties to even.
-  * scales are powers of two 2^e with e = ceil(log2(amax / 448)) (e = 0 when amax = 0), so
-    that the largest scaled magnitude lies in (224, 448]: Q per query row, K per token, the
-    pooled K per pooled row.
+  * scales are powers of two 2^e with e = ceil(log2(amax / 448)) (e = 0 when amax = 0; e kept
+    in [-127, 127], the range of the E8M0 scale code), so that the largest scaled magnitude
+    lies in (224, 448]: Q per query row, K per token, the pooled K per pooled row.
   * every logit (exact tokens and centroids) is the product of the dequantised Q and K rows;
     the softmax, the centroid multiplicities and the value products are those of the bf16
     pass, with V and the pooled V unquantised.
@@ -40,11 +40,12 @@ def e4m3_round(x):
 
 
 def scale_exp(amax):
-    """e = ceil(log2(amax / 448)), 0 for amax = 0: the power-of-two scale of a group."""
+    """e = ceil(log2(amax / 448)) in [-127, 127], 0 for amax = 0: the power-of-two scale of a
+    group."""
     amax = np.asarray(amax, dtype=np.float64)
     with np.errstate(divide="ignore"):
         e = np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / E4M3_MAX))
-    return np.where(amax > 0, e, 0.0)
+    return np.clip(np.where(amax > 0, e, 0.0), -127, 127)
 
 
 def quantize(x, e):

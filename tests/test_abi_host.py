@@ -143,6 +143,19 @@ def test_query_row_window_validation_and_layout():
     assert sa.workspace_bytes(0, sa.BF16, 1, 2, 4096, 64, 64, 64, 4097) == 0
 
 
+def test_fp8qk_layout():
+    assert check(opts=sa.make_opts(dtype=sa.BF16_FP8QK)) == sa.OK
+    assert check(opts=sa.make_opts(dtype=3)) == sa.EINVAL
+    bf = sa.workspace_layout(0, sa.BF16, 1, 2, 4096, 128, 64, 64)
+    f8 = sa.workspace_layout(0, sa.BF16_FP8QK, 1, 2, 4096, 128, 64, 64)
+    assert bf.k8 == 0 and bf.kb8 == 0
+    # the bf16 buffers are where they were; the E4M3 tiles follow them
+    assert (f8.qbar, f8.extra_flag, f8.v_t) == (bf.qbar, bf.extra_flag, bf.v_t)
+    tb = 64 * 128 + 64
+    assert f8.k8 >= bf.total - 255 and f8.kb8 - f8.k8 >= 2 * 64 * tb
+    assert f8.total - f8.kb8 >= 2 * 1 * tb
+
+
 def test_page_parameter_ranges_are_accepted():
     g = json.load(open(GOLDEN))
     assert check(extra=g["extra_tokens_range"]["max"]) == sa.OK

@@ -307,3 +307,72 @@ def test_finite_check_counts_nonfinite_values(dtype):
     n_out = int((~torch.isfinite(out.float())).sum().item())
     assert n_out > 0
     assert stats[7].item() == 3 + n_out
+
+
+@pytest.mark.parametrize("mode", ["sol", "sla", "local3d"])
+def test_fp8qk_flavour(mode):
+    # the fp8-QK flavour: the selection must be the bf16 path's, bit for bit, and the output
+    # within the bf16 tolerance of the fp8-QK oracle run on the GPU's selection and pooled keys
+    from oracle import fp8
+    bq = 128 if mode == "sla" else 64
+    w = workload(2, mode=mode, H=2, extra_tokens=128, dense_rows=(16384 - 1024, 16384),
+                 block_q=bq, keep_percent=15.0)
+    x = make_inputs(w)
+    q, k, v = device_inputs(x)
+    call = {"sol": sa.sol_attn, "sla": sa.sla_attn, "local3d": sa.local3d_attn}[mode]
+    kw = dict(block_q=bq, block_k=64, sink_range=w.sink_range, extra_tokens=w.extra_tokens,
+              dense_rows=w.dense_rows, return_workspace=True)
+    if mode == "sol":
+        kw["tau"] = w.tau
+    elif mode == "sla":
+        kw["keep_percent"] = w.keep_percent
+    else:
+        kw["grid"] = (w.T, w.Hh, w.Ww)
+    print(f"\n[fp8qk] {mode}: bf16 and fp8-QK calls", flush=True)
+    out_b, ws_b = call(q, k, v, **kw)
+    out_8, ws_8 = call(q, k, v, qk_fp8=True, **kw)
+    torch.cuda.synchronize()
+    m = {"sol": sa.MODE_SOL, "sla": sa.MODE_SLA, "local3d": sa.MODE_LOCAL3D}[mode]
+    vb = sa.selection_views(ws_b, m, sa.BF16, 1, w.H, w.N, w.d, bq, 64)
+    v8 = sa.selection_views(ws_8, m, sa.BF16_FP8QK, 1, w.H, w.N, w.d, bq, 64)
+    from parity import gpu_extra_sets, gpu_kept_mask
+    for name in ("kept_cnt", "extra_cnt", "mult"):
+        assert torch.equal(vb[name], v8[name]), name
+    sel = {k_: v_.cpu().numpy() for k_, v_ in v8.items()}
+    selb = {k_: v_.cpu().numpy() for k_, v_ in vb.items()}
+    for h in range(w.H):       # the lists' valid prefixes (the rest of each row is scratch)
+        np.testing.assert_array_equal(gpu_kept_mask(sel, h, w.N // 64), gpu_kept_mask(selb, h, w.N // 64))
+        for a_, b_ in zip(gpu_extra_sets(sel, h), gpu_extra_sets(selb, h)):
+            np.testing.assert_array_equal(a_, b_)
+    out8 = out_8.float().cpu().numpy().astype(np.float64)
+    worst = (0.0, 0.0)
+    for h in range(w.H):
+        xin = (x.q[0, h].astype(np.float64), x.k[0, h].astype(np.float64), x.v[0, h].astype(np.float64))
+        M = w.N // 64
+        gsel = (gpu_kept_mask(sel, h, M), gpu_extra_sets(sel, h))
+        ref = fp8.head_forward_fp8qk(mode, *xin, block_q=bq,
+                                     block_k=64, selection=gsel, dense_rows=w.dense_rows,
+                                     kbar=sel["kbar"][h].astype(np.float64))
+        err = np.abs(out8[0, h] - ref)
+        worst = (max(worst[0], float(err.max())), max(worst[1], float(err.mean())))
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, (h, err.max(), err.mean())
+    # not value-identical to the bf16 path, but close to it
+    d = (out_8.float() - out_b.float()).abs()
+    print(f"[fp8qk] {mode}: vs oracle max {worst[0]:.3e} mean {worst[1]:.3e}; vs bf16 path "
+          f"max {d.max().item():.3e} mean {d.mean().item():.3e}", flush=True)
+    assert d.max().item() > 0 and d.mean().item() < 0.05
+
+
+def test_fp8qk_chunked_equals_whole_call():
+    from block_sparse_attention_scores_amd.chunked import chunked_attention
+    w = workload(2, H=2, extra_tokens=128, dense_rows=(16384 - 1024, 16384))
+    x = make_inputs(w)
+    q, k, v = device_inputs(x)
+    pr = dict(tau=w.tau, sink_range=w.sink_range, extra_tokens=w.extra_tokens,
+              dense_rows=w.dense_rows, qk_fp8=True)
+    print("\n[fp8qk] chunked vs whole", flush=True)
+    ref = sa.sol_attn(q, k, v, **pr)
+    got, rep = chunked_attention("sol", q, k, v, chunk_rows=4096, **pr)
+    torch.cuda.synchronize()
+    assert len(rep.chunks) == 4
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))

@@ -60,6 +60,7 @@ def test_rounding_is_nearest_within_the_format_bounds():
 def test_scale_exponent_puts_the_group_max_in_the_top_binade():
     rng = np.random.default_rng(4)
     amax = 2.0 ** rng.uniform(-40, 40, 5000)
+    assert fp8.scale_exp(np.array([2.0 ** -200]))[0] == -127
     e = fp8.scale_exp(amax)
     s = amax / 2.0 ** e
     assert ((s > 224) & (s <= 448)).all()
