@@ -8,5 +8,5 @@ from ._lib import (  # noqa: F401
     FLAG_EXACT_EXTRA, FLAG_CHECK_FINITE, NSTATS, STAT_NAMES,
     SolattnError, Opts, WsLayout, lib, sol_attn, sla_attn, local3d_attn, workspace_layout, workspace_bytes,
     alloc_workspace, selection_views, status_string, last_error, kernel_names, timing_enable,
-    timing_read, make_opts, header_functions,
+    timing_read, make_opts, header_functions, pair_schedule, PAIR_STRIDES,
 )

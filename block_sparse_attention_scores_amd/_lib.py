@@ -20,6 +20,9 @@ MAX_EXTRA = 256
 NKERNELS = 5
 
 
+PAIR_STRIDES = 8           # candidate pairing strides of the bf16 attention kernel
+
+
 class SolattnError(RuntimeError):
     def __init__(self, status: int, detail: str):
         self.status = status
@@ -59,7 +62,7 @@ class WsLayout(ctypes.Structure):
         "total", "qbar", "kbar", "vbar", "scores", "kept_cnt", "kept_idx", "kept_bm", "mult", "cbias", "extra_cnt",
         "extra_idx", "extra_buf", "extra_part", "extra_flag", "kbar_bf", "vbar_t", "v_t")] + [
         ("Mq", ctypes.c_int), ("M", ctypes.c_int), ("Mpad", ctypes.c_int),
-        ("k8", ctypes.c_size_t), ("kb8", ctypes.c_size_t)]
+        ("k8", ctypes.c_size_t), ("kb8", ctypes.c_size_t), ("pair_plan", ctypes.c_size_t)]
 
 
 _lib = None
@@ -102,6 +105,9 @@ def lib() -> ctypes.CDLL:
     L.solattn_timing_read.restype = i
     L.solattn_kernel_name.argtypes = [i]
     L.solattn_kernel_name.restype = ctypes.c_char_p
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.solattn_pair_schedule.argtypes = [i, i, i, i, ip, ip, i]
+    L.solattn_pair_schedule.restype = i
     _lib = L
     return L
 
@@ -116,6 +122,18 @@ def last_error() -> str:
 
 def kernel_names():
     return [lib().solattn_kernel_name(k).decode() for k in range(NKERNELS)]
+
+
+def pair_schedule(Mq: int, dense=(0, 0), stride: int = 1):
+    """[(qa, qb), ...]: the query blocks of each unit of one head of the bf16 attention kernel
+    with 64-row query blocks (qb = -1: a single block), dense query blocks [dense[0], dense[1]),
+    under pairing `stride`."""
+    n = lib().solattn_pair_schedule(Mq, dense[0], dense[1], stride, None, None, 0)
+    if n < 0:
+        raise SolattnError(n, last_error())
+    qa, qb = (ctypes.c_int * max(n, 1))(), (ctypes.c_int * max(n, 1))()
+    lib().solattn_pair_schedule(Mq, dense[0], dense[1], stride, qa, qb, n)
+    return [(qa[j], qb[j]) for j in range(n)]
 
 
 def workspace_layout(mode: int, dtype: int, B: int, H: int, N: int, d: int, block_q: int,
@@ -302,7 +320,11 @@ def selection_views(workspace, mode, dtype, B, H, N, d, block_q, block_k, q_rows
         nbytes = count * torch.tensor([], dtype=dt).element_size()
         return workspace[off:off + nbytes].view(dt).reshape(shape)
 
+    extra = {}
+    if L.pair_plan:
+        extra["pair_plan"] = view(L.pair_plan, BH * PAIR_STRIDES, torch.int64, (BH, PAIR_STRIDES))
     return dict(
+        **extra,
         qbar=view(L.qbar, BH * Mq * d, torch.float32, (BH, Mq, d)),
         kbar=view(L.kbar, BH * M * d, torch.float32, (BH, M, d)),
         vbar=view(L.vbar, BH * M * d, torch.float32, (BH, M, d)),

@@ -177,6 +177,7 @@ int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int blo
     L->k8 = take(BH * (size_t)M * tb);
     L->kb8 = take(BH * (size_t)(Mpad / 64) * tb);
   }
+  if (dtype != SOLATTN_FP32 && block_q == 64) L->pair_plan = take(BH * solattn::PAIR_STRIDES * 8);
   L->total = off;
   L->Mq = Mq;
   L->M = M;
@@ -312,6 +313,7 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
     P.k8 = reinterpret_cast<uint8_t*>(ws + L.k8);
     P.kb8 = reinterpret_cast<uint8_t*>(ws + L.kb8);
   }
+  P.pair_plan = L.pair_plan ? reinterpret_cast<long long*>(ws + L.pair_plan) : nullptr;
 
   if (opts && opts->stats && L.extra_part - L.extra_buf < solattn::stats_scratch_bytes())
     return fail(SOLATTN_ENOTSUP, "stats: candidate buffer smaller than the counters' scratch");
@@ -356,6 +358,8 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
     }
     mark(2);
     if ((err = solattn::launch_block_select(P, stream)) != hipSuccess) return "block_select";
+    // the pairing of query blocks for the attention kernel; its time counts with the selection
+    if ((err = solattn::launch_pair_plan(P, stream)) != hipSuccess) return "pair_plan";
     tc.ran[2] = true;
     mark(3);
     if (do_extra) {
@@ -503,6 +507,18 @@ int solattn_timing_read(double* ms, long long* launches, int n) {
 const char* solattn_kernel_name(int index) {
   if (index < 0 || index >= NK) return "";
   return kKernelNames[index];
+}
+
+int solattn_pair_schedule(int Mq, int dense_q0, int dense_q1, int stride, int* qa, int* qb, int cap) {
+  g_err.clear();
+  if (Mq < 1 || dense_q0 < 0 || dense_q1 < dense_q0 || dense_q1 > Mq || stride < 1 ||
+      stride > solattn::PAIR_STRIDES || cap < 0 || (cap > 0 && (!qa || !qb)))
+    return fail(SOLATTN_EINVAL, "pair_schedule: invalid arguments");
+  if (dense_q1 == dense_q0) dense_q0 = dense_q1 = 0;
+  const int n = solattn::flash_units_per_head(2, Mq, dense_q1 - dense_q0);
+  for (int j = 0; j < n && j < cap; ++j)
+    solattn::flash_unit_blocks(2, Mq, dense_q0, dense_q1, stride, j, qa + j, qb + j);
+  return n;
 }
 
 }  // extern "C"

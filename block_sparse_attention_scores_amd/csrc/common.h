@@ -49,6 +49,8 @@ struct Problem {
   int extra_slices;      // token slices of the extra-token selection
   uint8_t* k8;           // fp8-QK: E4M3 key tiles [B*H, M] of 64*d bytes + 64 scale codes
   uint8_t* kb8;          // fp8-QK: E4M3 pooled-key tiles [B*H, Mpad/64], same layout
+  long long* pair_plan;  // [B*H, PAIR_STRIDES]: kept-block union summed over the pairs of each
+                         // pairing stride (bf16 kernel with 64-row query blocks; else null)
   uint16_t* kbar_bf;
   uint16_t* vbar_t;
   uint16_t* v_t;
@@ -63,6 +65,62 @@ constexpr int MAX_BLOCKS_BF16 = 64 * 64;
 // back to the best extra_tokens entries only when one more 32-token step could overflow it,
 // which for the workloads here almost never happens.
 constexpr int EXTRA_CAP = 1024;
+
+// Pairs of 64-row query blocks of the bf16 attention kernel (one pair per workgroup; the pair
+// walks the union of its two kept-block sets, so pairs whose sets overlap most waste least).
+// The dense query blocks [dq0, dq0 + nd) pair with their neighbours.  The other Ms = Mq - nd
+// blocks, numbered 0..Ms-1 in order with the dense run cut out, pair under a stride s chosen
+// per head: in each run of 2s blocks, block t pairs with block t + s; the blocks after the last
+// whole run pair with their neighbours.  Stride 1 is neighbour pairing.  A block's result does
+// not depend on its partner.
+constexpr int PAIR_STRIDES = 8;          // candidate strides 1..PAIR_STRIDES
+
+__host__ __device__ inline int flash_pairs_per_head(int Mq, int nd) {
+  return (nd + 1) / 2 + (Mq - nd + 1) / 2;
+}
+
+// The p-th pair (0 <= p < (Ms+1)/2) of the non-dense blocks under stride s, as query block
+// numbers; *b = -1 when the last block has no partner.
+__host__ __device__ inline void sparse_pair(int p, int s, int Ms, int dq0, int nd, int* a, int* b) {
+  const int C = Ms / (2 * s);                // whole runs of 2s blocks
+  int ia, ib;
+  if (p < C * s) {
+    const int c = p / s, t = p - c * s;
+    ia = 2 * s * c + t;
+    ib = ia + s;
+  } else {
+    ia = 2 * C * s + 2 * (p - C * s);
+    ib = ia + 1 < Ms ? ia + 1 : -1;
+  }
+  *a = ia < dq0 ? ia : ia + nd;
+  *b = ib < 0 ? -1 : (ib < dq0 ? ib : ib + nd);
+}
+
+// Work units of one head for the attention kernel with G query blocks per workgroup (G = 2:
+// pairs; G = 1: single blocks): the dense blocks' units first, then the others.
+__host__ __device__ inline int flash_units_per_head(int G, int Mq, int nd) {
+  return G == 2 ? flash_pairs_per_head(Mq, nd) : Mq;
+}
+__host__ __device__ inline int flash_dense_units(int G, int nd) {
+  return G == 2 ? (nd + 1) / 2 : nd;
+}
+
+// Query blocks of unit j (0 <= j < flash_units_per_head) of a head, dense query blocks
+// [dq0, dq1); stride: the head's pairing stride (G = 2).  *qb = -1 when the unit has one block.
+__host__ __device__ inline void flash_unit_blocks(int G, int Mq, int dq0, int dq1, int stride, int j,
+                                                  int* qa, int* qb) {
+  const int nd = dq1 - dq0, nu_d = flash_dense_units(G, nd);
+  if (j < nu_d) {
+    *qa = dq0 + j * G;
+    *qb = (G == 2 && *qa + 1 < dq1) ? *qa + 1 : -1;
+  } else if (G == 1) {
+    const int r = j - nu_d;
+    *qa = r < dq0 ? r : r + nd;
+    *qb = -1;
+  } else {
+    sparse_pair(j - nu_d, stride, Mq - nd, dq0, nd, qa, qb);
+  }
+}
 
 // Token slices of the extra-token selection: enough workgroups to fill the chip, at most 4.
 __host__ __device__ inline int extra_slice_count(int B, int H, int Mq) {

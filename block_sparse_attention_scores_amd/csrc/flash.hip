@@ -110,34 +110,41 @@ struct TileIter {
   }
 };
 
-// Workgroup -> (head, pair of query blocks).  Pairs overlapping the dense row range (the
-// heaviest) come first, then the rest head-major.  Consecutive units go to the same XCD in runs
-// of XCD_RUN (workgroups are dealt to the 8 XCDs round-robin), so one XCD works on neighbouring
-// query blocks of one head and shares their key tiles in its L2.
+// Workgroup -> (head, query blocks qa and qb of the workgroup; qb = -1 if none).  Units of the
+// dense query blocks (the heaviest) come first, then the rest head-major.  Consecutive units go
+// to the same XCD in runs of XCD_RUN (workgroups are dealt to the 8 XCDs round-robin), so one
+// XCD works on neighbouring query blocks of one head and shares their key tiles in its L2.
+// G = 2: pairs as sparse_pair() defines them, under the head's stride with the least total
+// kept-block union (the smallest such stride on ties); G = 1: one query block per workgroup.
 constexpr int XCD_RUN = 16;
 
-__device__ __forceinline__ bool flash_unit(const Problem& P, int G, int gid, int* bh, int* pair) {
+__device__ __forceinline__ bool flash_unit(const Problem& P, int G, int gid, int* bh, int* qa, int* qb) {
   const int x = gid % 8, k = gid / 8;
   const int u = (k / XCD_RUN) * 8 * XCD_RUN + x * XCD_RUN + (k % XCD_RUN);
-  const int Mp = (P.Mq + G - 1) / G;
   const int BH = P.B * P.H;
-  int h0 = 0, h1 = 0;
-  if (P.dense_q1 > P.dense_q0) {
-    h0 = P.dense_q0 / G;
-    h1 = (P.dense_q1 + G - 1) / G;
+  const int nd = P.dense_q1 - P.dense_q0;
+  const int nu_d = flash_dense_units(G, nd);
+  const int nu_s = flash_units_per_head(G, P.Mq, nd) - nu_d;
+  if (u >= BH * (nu_d + nu_s)) return false;
+  int j;
+  if (u < BH * nu_d) {
+    *bh = u / nu_d;
+    j = u % nu_d;
+  } else {
+    *bh = (u - BH * nu_d) / nu_s;
+    j = nu_d + (u - BH * nu_d) % nu_s;
   }
-  const int nh = h1 - h0;
-  if (u >= BH * Mp) return false;
-  if (u < BH * nh) {
-    *bh = u / nh;
-    *pair = h0 + u % nh;
-    return true;
+  int stride = 1;
+  if (G == 2 && j >= nu_d && P.pair_plan) {
+    const long long* tot = P.pair_plan + (size_t)*bh * PAIR_STRIDES;
+    long long best = tot[0];
+    for (int c = 1; c < PAIR_STRIDES; ++c)
+      if (tot[c] < best) {
+        best = tot[c];
+        stride = c + 1;
+      }
   }
-  const int v = u - BH * nh;
-  const int ns = Mp - nh;
-  *bh = v / ns;
-  const int r = v % ns;
-  *pair = r < h0 ? r : r + nh;
+  flash_unit_blocks(G, P.Mq, P.dense_q0, P.dense_q1, stride, j, qa, qb);
   return true;
 }
 
@@ -153,8 +160,8 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
   constexpr int KCH8 = D / 16;               // 16-byte chunks per E4M3 K row
   constexpr int PER_THREAD8 = 64 * D / 16 / 256;
   constexpr uint32_t TB8 = 64 * D + 64;      // E4M3 tile: rows, then the rows' scale codes
-  int bh, pair;
-  if (!flash_unit(P, G, blockIdx.x, &bh, &pair)) return;
+  int bh, qa, qb_;
+  if (!flash_unit(P, G, blockIdx.x, &bh, &qa, &qb_)) return;
   // the wave index is uniform: read it into a scalar so that every per-wave decision (which
   // query block, whether the wave works on a tile) is a scalar branch, not an exec mask
   const int tid = threadIdx.x, l = tid % 64, h32 = l / 32, c32 = l % 32;
@@ -172,9 +179,9 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
   const int* elist[2];
 #pragma unroll
   for (int gg = 0; gg < 2; ++gg) {
-    qb[gg] = pair * G + gg;
-    valid[gg] = gg < G && qb[gg] < P.Mq;
-    const int qq = valid[gg] ? qb[gg] : pair * G;
+    qb[gg] = gg == 0 ? qa : qb_;
+    valid[gg] = qb[gg] >= 0;
+    const int qq = valid[gg] ? qb[gg] : qa;
     const size_t row = (size_t)bh * P.Mq + qq;
     dense[gg] = qq >= P.dense_q0 && qq < P.dense_q1;
     nk[gg] = valid[gg] ? uniform(P.kept_cnt[row]) : 0;
@@ -183,7 +190,8 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
     kw[gg] = (valid[gg] && l < nwords) ? P.kept_bm[row * nwords + l] : 0ull;
     elist[gg] = P.extra_idx + row * MAX_EXTRA;
   }
-  const float* cbrow0 = P.cbias + ((size_t)bh * P.Mq + pair * G) * P.Mpad;
+  const float* cbrow[2] = {P.cbias + ((size_t)bh * P.Mq + qa) * P.Mpad,
+                           P.cbias + ((size_t)bh * P.Mq + (valid[1] ? qb[1] : qa)) * P.Mpad};
   int cent_sel = 0;
   if (P.mode == 0) {
 #pragma unroll
@@ -298,13 +306,15 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
         buf_to_lds16(vr, voff[u], vd + u * 4096);
       }
     }
-    if (t.kind == 2 && w == 0 && l < 32) {
-      // the 64 biases of both query blocks (consecutive rows): lanes 0-15 block 0, 16-31 block 1
-      const uint32_t nrec = static_cast<uint32_t>(
-          uniform((G == 2 && valid[1]) ? P.Mpad * 4 + 256 : 256));
-      const __amdgpu_buffer_rsrc_t br = make_rsrc(cbrow0 + t.idx, nrec);
-      buf_to_lds16(br, static_cast<uint32_t>(l >> 4) * static_cast<uint32_t>(P.Mpad) * 4u + (l & 15) * 16,
-                   reinterpret_cast<char*>(sm.bias[bf]));
+    if (t.kind == 2 && w == 0) {
+      // the 64 biases of each query block: lanes 0-15 those of block 0 into sm.bias[bf][0],
+      // lanes 16-31 those of block 1 into sm.bias[bf][1] (lane i's 16 bytes land at 16 i)
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) {
+        if (!valid[gg]) continue;
+        const __amdgpu_buffer_rsrc_t br = make_rsrc(cbrow[gg] + t.idx, 256);
+        if ((l >> 4) == gg) buf_to_lds16(br, (l & 15) * 16, reinterpret_cast<char*>(sm.bias[bf]));
+      }
     }
   };
 
@@ -676,8 +686,7 @@ __global__ __launch_bounds__(BQ) void sparse_flash_f32_kernel(Problem P) {
 hipError_t launch_sparse_flash(const Problem& P, hipStream_t stream) {
   if (P.dtype == 0) {
     const int G = P.bq == 64 ? 2 : 1;
-    const int Mp = (P.Mq + G - 1) / G;
-    const int units = P.B * P.H * Mp;
+    const int units = P.B * P.H * flash_units_per_head(G, P.Mq, P.dense_q1 - P.dense_q0);
     const int per_round = 8 * XCD_RUN;
     dim3 grid((units + per_round - 1) / per_round * per_round);
     if (P.fp8qk) {

@@ -8,6 +8,8 @@ hipError_t launch_block_pool(const Problem& P, hipStream_t stream);
 hipError_t launch_quantize_k(const Problem& P, hipStream_t stream);   // fp8-QK key tiles
 hipError_t launch_block_score(const Problem& P, hipStream_t stream);
 hipError_t launch_block_select(const Problem& P, hipStream_t stream);
+// Kept-block union of every pairing stride (bf16 kernel, 64-row query blocks only).
+hipError_t launch_pair_plan(const Problem& P, hipStream_t stream);
 hipError_t launch_extra_select(const Problem& P, hipStream_t stream);
 hipError_t launch_sparse_flash(const Problem& P, hipStream_t stream);
 // Per-call counters into stats[0..7] (see include/solattn.h); reuses extra_buf as scratch.

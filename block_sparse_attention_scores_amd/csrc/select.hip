@@ -216,6 +216,42 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
   }
 }
 
+// The tile steps a head's pairs of query blocks would take under pairing stride
+// s = blockIdx.y + 1: the kept-block union of each pair, summed (one workgroup per head and
+// stride; the threads stride over the (pair, bitmap word) index space, so that every lane
+// issues its own independent loads).
+__global__ __launch_bounds__(256) void pair_plan_kernel(Problem P) {
+  const int bh = blockIdx.x, s = blockIdx.y + 1;
+  const int nd = P.dense_q1 - P.dense_q0, Ms = P.Mq - nd, npair = (Ms + 1) / 2;
+  const int nw = P.Mpad / 64;
+  const uint64_t* bm = P.kept_bm + (size_t)bh * P.Mq * nw;
+  const int total = npair * nw;
+  int acc = 0;
+#pragma unroll 4
+  for (int e = threadIdx.x; e < total; e += 256) {
+    const int p = e / nw, w = e - p * nw;
+    int a, b;
+    sparse_pair(p, s, Ms, P.dense_q0, nd, &a, &b);
+    uint64_t x = bm[(size_t)a * nw + w];
+    if (b >= 0) x |= bm[(size_t)b * nw + w];
+    acc += __popcll(x);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  __shared__ int part[4];
+  if (threadIdx.x % 64 == 0) part[threadIdx.x / 64] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    P.pair_plan[(size_t)bh * PAIR_STRIDES + blockIdx.y] =
+        (long long)part[0] + part[1] + part[2] + part[3];
+}
+
+hipError_t launch_pair_plan(const Problem& P, hipStream_t stream) {
+  if (!P.pair_plan) return hipSuccess;
+  hipLaunchKernelGGL(pair_plan_kernel, dim3(P.B * P.H, PAIR_STRIDES), dim3(256), 0, stream, P);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_select(const Problem& P, hipStream_t stream) {
   dim3 grid(P.Mq, P.B * P.H);
   const size_t lds = P.mode == 2 ? (size_t)(P.Mpad / 32) * 4 : 0;

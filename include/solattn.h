@@ -228,6 +228,11 @@ int local3d_check_args(const void* q, const void* k, const void* v, void* out,
  *             [B*H, M, d, 64]: operand copies for the attention kernel (bf16 only)
  *   k8, kb8   E4M3 tiles [B*H, M] and [B*H, Mpad/64] of 64 * d bytes (64 rows) followed by
  *             the 64 rows' scale codes e + 127 (SOLATTN_BF16_FP8QK only)
+ *   pair_plan int64 [B*H, 8]: for pairing strides s = 1..8, the kept-block union summed over
+ *             the pairs of query blocks that one attention workgroup takes together (with
+ *             stride s, block t of each run of 2s non-dense query blocks pairs with block t+s);
+ *             each head's workgroups use the stride with the least sum.  Scheduling only: no
+ *             output depends on it (bf16 tensors with block_q 64 only; offset 0 otherwise)
  * Mq = N/block_q, M = N/block_k, Mpad = M rounded up to a multiple of 64.
  */
 typedef struct solattn_ws_layout {
@@ -238,6 +243,8 @@ typedef struct solattn_ws_layout {
   size_t kbar_bf, vbar_t, v_t;
   int Mq, M, Mpad;
   size_t k8, kb8;                /* SOLATTN_BF16_FP8QK only: E4M3 key and pooled-key tiles  */
+  size_t pair_plan;              /* 16-bit types with block_q 64 only (else 0): int64
+                                    [B*H, 8], see above                                      */
 } solattn_ws_layout;
 
 /* Fills *layout for a call of this shape.  Returns SOLATTN_OK or SOLATTN_EINVAL. */
@@ -260,6 +267,20 @@ const char* solattn_status_string(int status);
 
 /* Thread-local detail of the last failing call on this thread ("" if none). */
 const char* solattn_last_error(void);
+
+/*
+ * Scheduling of the bf16 attention kernel with 64-row query blocks (host only, no device
+ * call): the query blocks of each workgroup-sized unit of one head, in unit order, for Mq
+ * query blocks of which [dense_q0, dense_q1) are dense and pairing stride `stride` (1..8; the
+ * kernel takes, per head, the stride with the least sum in the workspace's pair_plan).  The
+ * dense blocks' units come first, paired with their neighbours; the other blocks, numbered in
+ * order with the dense run cut out, pair block t with block t + stride in each run of
+ * 2 * stride of them, and the blocks after the last whole run pair with their neighbours.
+ * Fills qa[j], qb[j] (qb[j] = -1: a single block) for j < min(units, cap) and returns the
+ * number of units, or SOLATTN_EINVAL.  The pairing decides only which query blocks share a
+ * workgroup (and so a walk over the union of their kept blocks); no result depends on it.
+ */
+int solattn_pair_schedule(int Mq, int dense_q0, int dense_q1, int stride, int* qa, int* qb, int cap);
 
 /*
  * Per-kernel timing.  While enabled, every call records HIP events around each

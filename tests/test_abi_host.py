@@ -152,8 +152,19 @@ def test_fp8qk_layout():
     # the bf16 buffers are where they were; the E4M3 tiles follow them
     assert (f8.qbar, f8.extra_flag, f8.v_t) == (bf.qbar, bf.extra_flag, bf.v_t)
     tb = 64 * 128 + 64
-    assert f8.k8 >= bf.total - 255 and f8.kb8 - f8.k8 >= 2 * 64 * tb
-    assert f8.total - f8.kb8 >= 2 * 1 * tb
+    v_t_bytes = 2 * 64 * 128 * 64 * 2
+    assert f8.k8 >= bf.v_t + v_t_bytes and f8.kb8 - f8.k8 >= 2 * 64 * tb
+    assert f8.pair_plan - f8.kb8 >= 2 * 1 * tb
+
+
+def test_pair_plan_layout():
+    # the pairing sums exist for the 16-bit kernel with 64-row query blocks only
+    bf = sa.workspace_layout(0, sa.BF16, 1, 2, 4096, 128, 64, 64)
+    assert bf.pair_plan > bf.v_t and bf.total - bf.pair_plan >= 2 * sa.PAIR_STRIDES * 8
+    assert bf.pair_plan % 256 == 0
+    assert sa.workspace_layout(0, sa.FP32, 1, 2, 4096, 128, 64, 64).pair_plan == 0
+    assert sa.workspace_layout(1, sa.BF16, 1, 2, 4096, 128, 128, 64).pair_plan == 0
+    assert sa.workspace_layout(0, sa.BF16_FP8QK, 1, 2, 4096, 128, 64, 64).pair_plan > 0
 
 
 def test_page_parameter_ranges_are_accepted():

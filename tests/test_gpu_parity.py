@@ -13,7 +13,7 @@ import torch
 import block_sparse_attention_scores_amd as sa
 from gen import Inputs, Workload, bf16_round, bf16_to_f32, make_inputs, random_qkv, workload
 from oracle import dense, solattn
-from parity import Report, check_head, device_inputs, run_gpu
+from parity import Report, check_head, device_inputs, gpu_kept_mask, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -99,6 +99,26 @@ def test_sol_long_n203k_all_heads():
     w = workload(5)
     x = make_inputs(w)
     run_and_check(w, x, [5], qblocks=_sample(50, n_sparse=4))
+
+
+def test_pairing_stride_on_a_96_wide_grid():
+    # 64-token blocks straddle the rows of a 96-token-wide grid, so a block's kept set overlaps
+    # most with the block three on (one grid row down), not with its neighbour: the attention
+    # kernel must pick stride 3 and still compute every query block, across a dense run of
+    # odd start and length
+    w = workload(2, T=2, Hh=96, Ww=96, extra_tokens=64, dense_rows=(64 * 101, 64 * 110))
+    x = make_inputs(w, heads=[0, 5])
+    out, sel, rep = run_and_check(w, x, range(2))      # every output row against the oracle
+    Mq, M = w.N // 64, w.N // 64
+    for bh in range(2):
+        kept = gpu_kept_mask(sel, bh, M)
+        tot = []
+        for s in range(1, sa.PAIR_STRIDES + 1):
+            units = sa.pair_schedule(Mq, (101, 110), s)[5:]     # the 5 dense units first
+            tot.append(sum(int((kept[a] | kept[b]).sum()) if b >= 0 else int(kept[a].sum())
+                           for a, b in units))
+        np.testing.assert_array_equal(sel["pair_plan"][bh], tot)
+        assert int(np.argmin(tot)) + 1 == 3, tot
 
 
 @pytest.mark.parametrize("extra", [0, 64])
