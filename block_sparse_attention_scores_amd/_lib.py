@@ -62,7 +62,8 @@ class WsLayout(ctypes.Structure):
         "total", "qbar", "kbar", "vbar", "scores", "kept_cnt", "kept_idx", "kept_bm", "mult", "cbias", "extra_cnt",
         "extra_idx", "extra_buf", "extra_part", "extra_flag", "kbar_bf", "vbar_t", "v_t")] + [
         ("Mq", ctypes.c_int), ("M", ctypes.c_int), ("Mpad", ctypes.c_int),
-        ("k8", ctypes.c_size_t), ("kb8", ctypes.c_size_t), ("pair_plan", ctypes.c_size_t)]
+        ("k8", ctypes.c_size_t), ("kb8", ctypes.c_size_t), ("pair_plan", ctypes.c_size_t),
+        ("extra_seed", ctypes.c_size_t)]
 
 
 _lib = None

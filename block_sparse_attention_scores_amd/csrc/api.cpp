@@ -163,9 +163,10 @@ int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int blo
   L->cbias = take(BH * Mq * Mpad * 4);
   L->extra_cnt = take(BH * Mq * 4);
   L->extra_idx = take(BH * Mq * SOLATTN_MAX_EXTRA * 4);
-  const int S = solattn::extra_slice_count(B, H, Mq);
-  L->extra_buf = take(BH * Mq * S * 4 * solattn::EXTRA_CAP * 8);
-  L->extra_part = take(BH * Mq * S * 4 * 4);
+  int S, nl;
+  solattn::extra_split(dtype == SOLATTN_FP32, B, H, Mq, &S, &nl);
+  L->extra_buf = take(BH * Mq * nl * solattn::EXTRA_CAP * 8);
+  L->extra_part = take(BH * Mq * nl * 4);
   L->extra_flag = take(BH * Mq * 4);
   if (dtype != SOLATTN_FP32) {
     L->kbar_bf = take(BH * Mpad * d * 2);
@@ -178,6 +179,7 @@ int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int blo
     L->kb8 = take(BH * (size_t)(Mpad / 64) * tb);
   }
   if (dtype != SOLATTN_FP32 && block_q == 64) L->pair_plan = take(BH * solattn::PAIR_STRIDES * 8);
+  L->extra_seed = take(BH * Mq * 4);
   L->total = off;
   L->Mq = Mq;
   L->M = M;
@@ -303,7 +305,8 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   P.extra_buf = reinterpret_cast<uint2*>(ws + L.extra_buf);
   P.extra_part = reinterpret_cast<int*>(ws + L.extra_part);
   P.extra_flag = reinterpret_cast<int*>(ws + L.extra_flag);
-  P.extra_slices = solattn::extra_slice_count(B, H, L.Mq);
+  solattn::extra_split(dtype == SOLATTN_FP32, B, H, L.Mq, &P.extra_slices, &P.extra_lists);
+  P.extra_seed = reinterpret_cast<uint32_t*>(ws + L.extra_seed);
   if (dtype != SOLATTN_FP32) {
     P.kbar_bf = reinterpret_cast<uint16_t*>(ws + L.kbar_bf);
     P.vbar_t = reinterpret_cast<uint16_t*>(ws + L.vbar_t);

@@ -43,8 +43,10 @@ struct Problem {
   float* cbias;          // ln(centroid multiplicity) / scale (a raw-score offset), -inf where it is 0
   int* extra_cnt;
   int* extra_idx;
-  uint2* extra_buf;      // per query block, token slice and wave: (score bits, token) candidates
-  int* extra_part;       // per query block, token slice and wave: entries left after the final cut
+  uint2* extra_buf;      // per query block and candidate list: (score bits, token) candidates
+  int* extra_part;       // per query block and candidate list: entries left after the final cut
+  uint32_t* extra_seed;  // per query block: seeded threshold key of the extra-token selection
+  int extra_lists;       // candidate lists per query block (extra_buf rows hold this many)
   int* extra_flag;       // per query block: 1 when the seeded threshold left too few candidates
   int extra_slices;      // token slices of the extra-token selection
   uint8_t* k8;           // fp8-QK: E4M3 key tiles [B*H, M] of 64*d bytes + 64 scale codes
@@ -122,11 +124,23 @@ __host__ __device__ inline void flash_unit_blocks(int G, int Mq, int dq0, int dq
   }
 }
 
-// Token slices of the extra-token selection: enough workgroups to fill the chip, at most 4.
-__host__ __device__ inline int extra_slice_count(int B, int H, int Mq) {
-  const long groups = (long)((Mq + 31) / 32) * B * H;
-  long s = (1536 + groups - 1) / groups;
-  return s < 1 ? 1 : (s > 4 ? 4 : (int)s);
+// Query blocks per workgroup of the extra-token selection's first pass: 128 for 16-bit tensors
+// (four waves of 32 that share each key tile staged in LDS), 32 for fp32 (four waves that take
+// turns over the token steps of the same 32 blocks).
+constexpr int EXTRA_GROUP_BF16 = 128;
+constexpr int EXTRA_GROUP_F32 = 32;
+
+// Token slices of the extra-token selection and candidate lists per query block.  16-bit: enough
+// slices for about 2048 workgroups (at most 16), one list per slice; fp32: enough for 1536 (at
+// most 4), one list per slice and wave.
+__host__ __device__ inline void extra_split(bool f32, int B, int H, int Mq, int* slices, int* lists) {
+  const int grp = f32 ? EXTRA_GROUP_F32 : EXTRA_GROUP_BF16;
+  const long groups = (long)((Mq + grp - 1) / grp) * B * H;
+  const long want = f32 ? 1536 : 2048, cap = f32 ? 4 : 16;
+  long s = (want + groups - 1) / groups;
+  s = s < 1 ? 1 : (s > cap ? cap : s);
+  *slices = (int)s;
+  *lists = f32 ? 4 * (int)s : (int)s;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -158,6 +172,33 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // instruction (given the 32x32 accumulator layout of the score tile) sit next to each other.
 __host__ __device__ __forceinline__ int vt_pos(int kk) {
   return (kk & ~0xC) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+}
+
+// ---- staging of key tiles in LDS (the attention kernel and the extra-token selection)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Asynchronous 16-byte global -> LDS copy through a buffer resource: lane l's 16 bytes land at
+// `wave_dst` + 16*l (the same `wave_dst` for the whole wave); `voff` is the lane's byte offset
+// from the resource base.  Out-of-range offsets read zero.
+__device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* wave_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(wave_dst), 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// LDS swizzle of bf16 key rows: the 16-byte chunk c of row r is stored at chunk position
+// kswz(r, c), so that any 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte
+// bank groups.  An involution in c: loading global chunk kswz(r, p) into position p stores it
+// where it belongs.
+template <int D>
+__host__ __device__ __forceinline__ int kswz(int r, int c) {
+  if constexpr (D == 128) return c ^ (r & 15);        // 256-byte rows
+  else return c ^ ((r >> 1) & 7);                     // 128-byte rows
 }
 
 // E4M3 scaling (the fp8-QK flavour): e = the smallest integer with amax <= 448 * 2^e

@@ -3,23 +3,25 @@
 // docs, common inputs table, extra_tokens row: extra high-score tokens each query block
 // attends beyond its selected blocks).
 //
-// Pass 1 (extra_select_kernel).  A workgroup of 4 waves owns 32 query blocks of one head and one
-// slice of the token range; the waves take turns over 32-token steps.  Scores come from the
-// 32x32x16 bf16 matrix instruction with q̄ split into two bf16 parts (hi + lo), accurate to
-// ~2^-17 relative (fp32-like), while the keys are exact bf16.  Each lane owns one query block
-// (a column of the accumulator).  Every wave keeps its own candidate buffer per query block in
-// the workspace, so the streaming loop needs no barrier; the four waves share one running
-// threshold per query block in LDS (any wave's E-th best is a lower bound of the final E-th
-// best).  A score above the threshold is appended; when a buffer could overflow on the next
-// step, the wave finds its E-th best entry by radix selection on (score, token), cuts the
-// buffer to exactly E entries and raises the shared threshold.  Keys stream in increasing token
-// order within a wave, so a later token that ties the threshold loses the tie and a strict
-// comparison suffices.
+// Pass 1 keeps, per query block, every key whose score reaches a running threshold, in
+// candidate lists in the workspace.  The threshold starts from a seed taken from a sample of
+// the keys and rises whenever a list is cut back to its E best entries (by radix selection on
+// (score, token)): any list's E-th best is a lower bound of the final E-th best, so no key of
+// the final selection is ever dropped.
+//   16-bit tensors (extra_seed_kernel, extra_tile_kernel): scores come from the 32x32x16 bf16
+//   matrix instruction with q̄ split into two bf16 parts (hi + lo), accurate to ~2^-17
+//   relative (fp32-like), while the keys are exact bf16; a workgroup owns 128 query blocks and
+//   shares key tiles staged in LDS among them (described below).
+//   fp32 (extra_select_kernel): a workgroup of 4 waves owns 32 query blocks of one head and one
+//   slice of the token range; the waves take turns over 32-token steps with exact fp32 dot
+//   products, each wave with its own candidate list per query block and one shared threshold
+//   per query block in LDS.
 //
 // Pass 2 (extra_merge_kernel).  One wave per query block takes the best E of the partial lists
 // (one per wave and slice), ranks them by token, writes them out, and takes the chosen tokens
 // out of their blocks' centroid terms.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "launch.h"
@@ -29,13 +31,10 @@ namespace solattn {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int XR = 32;      // query blocks per workgroup
+constexpr int XR = EXTRA_GROUP_F32;   // query blocks per workgroup (fp32 first pass)
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 constexpr int XSTEP = 32;   // tokens per wave step
 
 __device__ __forceinline__ void wave_sync() {
@@ -205,15 +204,15 @@ __device__ __forceinline__ int sample_run(int s, int nsteps, int M) {
   return j * 64 + ((nsteps > M) ? 32 * (s & 1) : 0);
 }
 
-// Pass 1.  repair = 0: every sparse query block, with thresholds seeded from the sample.
+// Pass 1, fp32.  repair = 0: every sparse query block, with thresholds seeded from the sample.
 // repair = 1: only the query blocks the merge flagged (fewer candidates than it needs), with
 // the threshold at its minimum, so that every candidate competes (the exact selection).
-template <typename T, int D>
+template <int D>
 __global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P, int repair) {
   __shared__ uint32_t thr[XR];            // shared threshold keys: append when key >= thr
   __shared__ int whist[4][256];
   __shared__ int wscr[4][4];
-  __shared__ float qs[(sizeof(T) == 4) ? XR : 1][D];
+  __shared__ float qs[XR][D];
   __shared__ uint32_t samp[XR][8 * SAMPLE_KEEP];   // per query block: the best sample keys of 8 lanes
   __shared__ int scnt[XR];                          // sample candidates per query block
   __shared__ int any_row;
@@ -237,77 +236,34 @@ __global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P, int rep
     if (!any_row) return;
   }
   const uint8_t* mrow = P.mult + grow * P.Mpad;
-  const T* kbase = static_cast<const T*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)h * P.k.sh;
+  const float* kbase = static_cast<const float*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)h * P.k.sh;
   const int ts = (((N + S - 1) / S) + 127) / 128 * 128;       // tokens per slice
   const int t_lo = slice * ts, t_hi = min(N, t_lo + ts);
 
   if (tid < XR) thr[tid] = 0u;
 
-  // q̄ operands: split bf16 hi/lo fragments (bf16 inputs) or an fp32 copy in LDS
-  bf16x8_t qhi[D / 16], qlo[D / 16];
-  if constexpr (sizeof(T) == 2) {
-    const float* qb = P.qbar + grow * D;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (i < P.Mq) ? qb[16 * ks + 8 * (l / 32) + e] : 0.f;
-        const uint16_t hb = f32_to_bf16(x);
-        const uint16_t lb = f32_to_bf16(x - bf16_to_f32(hb));
-        qhi[ks][e] = __builtin_bit_cast(__bf16, hb);
-        qlo[ks][e] = __builtin_bit_cast(__bf16, lb);
-      }
-    }
-  } else {
-    for (int u = tid; u < XR * D; u += 256) {
-      const int r = u / D, e = u % D;
-      qs[r][e] = (i0 + r < P.Mq) ? P.qbar[((size_t)bh * P.Mq + i0 + r) * D + e] : 0.f;
-    }
+  // q̄ of the group's query blocks, in LDS
+  for (int u = tid; u < XR * D; u += 256) {
+    const int r = u / D, e = u % D;
+    qs[r][e] = (i0 + r < P.Mq) ? P.qbar[((size_t)bh * P.Mq + i0 + r) * D + e] : 0.f;
   }
   __syncthreads();
 
   // scores of 32 consecutive tokens from tw for this lane's query block: register r holds token
-  // tw + (r/4)*8 + (l/32)*4 + r%4
-  // (bf16: the key fragments come from kf, loaded by load_keys, which first loads the step's
-  // candidate flag into mflag, so that waiting for the flag never waits for the keys)
-  bf16x8_t kf[D / 16];
+  // tw + (r/4)*8 + (l/32)*4 + r%4 (the layout of the 16-bit pass's accumulator)
   uint8_t mflag = 0;
-  auto load_keys = [&](int tw) {
-    mflag = row_ok ? mrow[tw >> 6] : 0;
-    if constexpr (sizeof(T) == 2) {
-      const T* kr = kbase + (int64_t)(tw + rl) * P.k.sn + 8 * (l / 32);
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) kf[ks] = *reinterpret_cast<const bf16x8_t*>(kr + 16 * ks);
-    }
-  };
-  // `prefetch(kc)` runs after this step's key fragments are copied out of kf (bf16), so the
-  // next step's loads can go out before this step's products
+  auto load_keys = [&](int tw) { mflag = row_ok ? mrow[tw >> 6] : 0; };
   auto scores = [&](int tw, float* acc, auto&& prefetch) {
-    if constexpr (sizeof(T) == 2) {
-      bf16x8_t kc[D / 16];
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) kc[ks] = kf[ks];
-      prefetch();
-      f32x16_t c = {};
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[ks], qhi[ks], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[ks], qlo[ks], c, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = c[r];
-    } else {
 #pragma unroll 1
-      for (int r = 0; r < 16; ++r) {
-        const int tk = tw + (r / 4) * 8 + (l / 32) * 4 + (r % 4);
-        const float* kr = reinterpret_cast<const float*>(kbase) + (int64_t)tk * P.k.sn;
-        float sc = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      const int tk = tw + (r / 4) * 8 + (l / 32) * 4 + (r % 4);
+      const float* kr = kbase + (int64_t)tk * P.k.sn;
+      float sc = 0.f;
 #pragma unroll 8
-        for (int e = 0; e < D; ++e) sc = fmaf(qs[rl][e], kr[e], sc);
-        acc[r] = sc;
-      }
-      prefetch();
+      for (int e = 0; e < D; ++e) sc = fmaf(qs[rl][e], kr[e], sc);
+      acc[r] = sc;
     }
+    prefetch();
   };
 
   if (!repair) {
@@ -373,7 +329,7 @@ __global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P, int rep
   const uint32_t row_stride = (uint32_t)S * 4u * EXTRA_CAP * 8u;        // bytes between query blocks
   const int nvalid = min(XR, P.Mq - i0);
   const __amdgpu_buffer_rsrc_t brsrc =
-      xrsrc(P.extra_buf + (((size_t)bh * P.Mq + i0) * S + slice) * 4 * EXTRA_CAP + (size_t)w * EXTRA_CAP,
+      make_rsrc(P.extra_buf + (((size_t)bh * P.Mq + i0) * S + slice) * 4 * EXTRA_CAP + (size_t)w * EXTRA_CAP,
             (uint32_t)(nvalid - 1) * row_stride + EXTRA_CAP * 8u);
   const uint32_t my_off = (uint32_t)rl * row_stride;
   // fill of this wave's buffer for the lane's query block; lanes l and l+32 share the block
@@ -440,6 +396,411 @@ __global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P, int rep
   }
 }
 
+// ---------------------------------------------------------------------- 16-bit first pass
+//
+// A workgroup owns EXTRA_GROUP_BF16 = 128 query blocks of one head (wave w: blocks
+// i0 + 32w .. i0 + 32w + 31, one per accumulator column) and one token slice.  Key tiles of
+// XTOK = 64 tokens are copied into LDS with buffer-to-LDS loads (chunk-swizzled rows) and read by
+// all four waves as the A operand, so every key byte fetched serves 128 query blocks.  XNB
+// buffers keep XNB - 1 tiles in flight: the wait before a tile leaves the later tiles' copies
+// outstanding (loads complete in issue order) and the barrier after it orders LDS only, so
+// nothing drains the queue.  A query block belongs to one wave, so its threshold lives in
+// registers; its candidates go to the list of its (query block, slice), stored one tile late
+// so that the stores complete while the next tile is scored.  The seeded thresholds come from
+// extra_seed_kernel, once per query block for all slices.
+
+constexpr int XTOK = 64;                   // tokens per key tile (2 steps of 32)
+constexpr int XNB = 4;                     // LDS tile buffers
+
+template <int D>
+struct ExtraSmem {
+  uint16_t k[XNB][XTOK * D];
+  uint32_t fl[XNB][2][256];  // per tile and run: each thread's kept-bitmap dword of the run's block
+  int hist[4][256];
+  int scr[4][4];
+  int any;
+};
+
+// Barrier for the tile loop: every wave has waited for its own copies of the tile (vmcnt), so
+// after it the whole tile is in LDS; the memory clobber keeps LDS accesses on their side.  No
+// memory fence: a fence would wait for every outstanding copy, including the later tiles'.
+__device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Wait until at most `later` tiles' copies (OPS per tile and thread) are outstanding.
+template <int OPS>
+__device__ __forceinline__ void wait_tiles(int later) {
+  if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * OPS) : "memory");
+  else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Asynchronous 4-byte global -> LDS copy with a scalar offset: lane l's dword lands at
+// `wave_dst` + 4*l.
+__device__ __forceinline__ void buf_to_lds4s(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                             void* wave_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(wave_dst), 4, voff, soff, 0, 0);
+}
+
+// Asynchronous 4-byte global -> LDS copy: lane l's dword lands at `wave_dst` + 4*l.
+__device__ __forceinline__ void buf_to_lds4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* wave_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(wave_dst), 4, voff, 0, 0, 0);
+}
+
+// Candidate flags travel with the key tiles: each thread copies the dword of its query block's
+// kept bitmap that holds key block j (a block is a candidate source when its bit is clear).
+struct FlagCopy {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t row_off;                        // byte offset of the lane's bitmap row (past the end if none)
+  __device__ void init(const Problem& P, int bh, int i) {
+    const uint32_t nwb = static_cast<uint32_t>(P.Mpad / 64) * 8u;
+    rs = make_rsrc(P.kept_bm + (size_t)bh * P.Mq * (P.Mpad / 64), static_cast<uint32_t>(P.Mq) * nwb);
+    row_off = static_cast<uint32_t>(i < P.Mq ? i : P.Mq) * nwb;
+  }
+  __device__ void issue(int j, uint32_t* dst) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    buf_to_lds4(rs, row_off + static_cast<uint32_t>(j >> 5) * 4u, dst + 64 * w);
+  }
+  __device__ static bool kept(const uint32_t* src, int j) {
+    return (src[threadIdx.x] >> (j & 31)) & 1u;
+  }
+};
+
+// The per-lane part shared by the two kernels: q̄ split into bf16 hi + lo fragments for this
+// lane's query block (zero past the last one), the tile loader and the score products.
+template <int D>
+struct ExtraTiles {
+  static constexpr int KCH = D / 8;                    // 16-byte chunks per key row
+  static constexpr int PT = XTOK * KCH / 256;          // chunk copies per thread per tile
+  bf16x8_t qhi[D / 16], qlo[D / 16];
+  uint32_t ak;                                         // lane's A-fragment byte offset in a 32-row step
+  uint32_t ksn_b;
+
+  __device__ void init(const Problem& P, size_t row, bool has_row) {
+    const float* qb = P.qbar + row * D;
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = has_row ? qb[16 * ks + 8 * (l / 32) + e] : 0.f;
+        const uint16_t hb = f32_to_bf16(x);
+        const uint16_t lb = f32_to_bf16(x - bf16_to_f32(hb));
+        qhi[ks][e] = __builtin_bit_cast(__bf16, hb);
+        qlo[ks][e] = __builtin_bit_cast(__bf16, lb);
+      }
+    }
+    const int c32 = l % 32, h32 = l / 32;
+    ak = c32 * (D * 2) + 16 * kswz<D>(c32, h32);
+    ksn_b = static_cast<uint32_t>(P.k.sn) * 2u;
+  }
+
+  // Copy key rows into `dst`: the tile is 2 runs of 32 rows; run(q) gives the first key row of
+  // run q and the bytes its buffer resource covers (rows past them read zero).
+  template <typename Run>
+  __device__ void issue(uint16_t* dst, Run&& run) {
+    const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int s = (u * 4 + w) * 64 + l;               // 16-byte slot; the wave's 64 slots are
+      const int r = s / KCH, c = s % KCH;               // rows of one run (4 or 8 rows)
+      const auto rb = run((u * 4 + w) * 64 / KCH / 32);
+      // the byte count is uniform but may be computed in a vector register: read it into a
+      // scalar one, or every copy would be wrapped in a loop over distinct resources
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(rb.first, static_cast<uint32_t>(uniform(static_cast<int>(rb.second))));
+      buf_to_lds16(rs, static_cast<uint32_t>(r % 32) * ksn_b + kswz<D>(r, c) * 16,
+                   reinterpret_cast<char*>(dst) + (u * 4 + w) * 1024);
+    }
+  }
+
+  // Scores of the 32 tokens of step q (rows 32q..32q+31 of the tile) for this lane's query
+  // block: register r holds token 32q + (r/4)*8 + (l/32)*4 + r%4.
+  __device__ f32x16_t scores(const uint16_t* tile, int q) const {
+    const char* base = reinterpret_cast<const char*>(tile) + q * 32 * D * 2;
+    f32x16_t c = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(base + (ak ^ (32u * ks)));
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qhi[ks], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qlo[ks], c, 0, 0, 0);
+    }
+    return c;
+  }
+};
+
+// Workgroup -> (unit, query-block group) with every group of one unit on one XCD (workgroups
+// are dealt to the 8 XCDs round-robin): the groups of a unit read the same keys, so they share
+// them in that XCD's L2.  Returns false for the padding workgroups of the last round.
+__device__ __forceinline__ bool xcd_unit(int units, int ngrp, int* unit, int* grp) {
+  const int id = blockIdx.x, x = id % 8, k = id / 8;
+  *unit = (k / ngrp) * 8 + x;
+  *grp = k % ngrp;
+  return *unit < units;
+}
+__host__ __device__ inline int xcd_grid(int units, int ngrp) { return (units + 7) / 8 * 8 * ngrp; }
+
+// Seeds: the sample runs (sample_run) scored for the group's 128 query blocks, two runs per
+// tile.  Each lane keeps the SAMPLE_KEEP best keys of every fourth run (four lists), so a query
+// block's two lanes hold 64 of its best sample keys; the seed is the r-th best of them, with r
+// chosen so that about SAMPLE_MARGIN * E candidates are expected at or above it.  A best-of-a-
+// subset is at most the best of the whole sample, so the seed only errs low (more candidates).
+template <int D>
+__global__ __launch_bounds__(256, 2) void extra_seed_kernel(Problem P) {
+  __shared__ ExtraSmem<D> sm;
+  using TT = ExtraTiles<D>;
+  int bh, grp;
+  if (!xcd_unit(P.B * P.H, (P.Mq + EXTRA_GROUP_BF16 - 1) / EXTRA_GROUP_BF16, &bh, &grp)) return;
+  const int tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int rl = l % 32, i = grp * EXTRA_GROUP_BF16 + 32 * w + rl;
+  const int b = bh / P.H, h = bh % P.H;
+  const size_t row = (size_t)bh * P.Mq + (i < P.Mq ? i : 0);
+  const bool row_ok = i < P.Mq && !(i >= P.dense_q0 && i < P.dense_q1);
+  const uint16_t* kbase = static_cast<const uint16_t*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)h * P.k.sh;
+  TT T;
+  T.init(P, row, i < P.Mq);
+  FlagCopy F;
+  F.init(P, bh, i);
+  const bool wave_on = __ballot(row_ok) != 0;
+
+  const int nsteps = min(2 * P.M, min(4 * SAMPLE_STEPS, max(SAMPLE_STEPS, P.N / 1024)));
+  const int ntile = (nsteps + 1) / 2;
+  auto run_tok = [&](int s) { return sample_run(s < nsteps ? s : 0, nsteps, P.M); };
+  constexpr int OPS = TT::PT + 2;          // copies per thread per tile: keys, two flag dwords
+  auto issue = [&](int it) {
+    T.issue(sm.k[it % XNB], [&](int q) {
+      return std::make_pair(kbase + (int64_t)run_tok(2 * it + q) * P.k.sn, 32u * T.ksn_b);
+    });
+#pragma unroll
+    for (int q = 0; q < 2; ++q) F.issue(run_tok(2 * it + q) >> 6, sm.fl[it % XNB][q]);
+  };
+  uint32_t best[4][SAMPLE_KEEP];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < SAMPLE_KEEP; ++e) best[q][e] = 0u;
+  int nsamp = 0;
+  for (int it = 0; it < XNB - 1 && it < ntile; ++it) issue(it);
+#pragma unroll 1
+  for (int it = 0; it < ntile; ++it) {
+    wait_tiles<OPS>(min(XNB - 2, ntile - 1 - it));
+    tile_barrier();
+    bool fl[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int s = 2 * it + q;
+      fl[q] = row_ok && s < nsteps && !FlagCopy::kept(sm.fl[it % XNB][q], run_tok(s) >> 6);
+    }
+    // every wave has read this tile's flags before the tile's buffer is refilled (a tile later)
+    if (it + XNB - 1 < ntile) issue(it + XNB - 1);
+    if (wave_on) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const f32x16_t c = T.scores(sm.k[it % XNB], q);
+        if (fl[q]) {
+          nsamp += 16;
+          // run 2 it + q goes to list (2 it + q) % 4
+          auto put = [&](uint32_t* bl) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              uint32_t k = float_key(c[r]);
+#pragma unroll
+              for (int e = 0; e < SAMPLE_KEEP; ++e) {
+                const uint32_t hi = max(bl[e], k), lo = min(bl[e], k);
+                bl[e] = hi;
+                k = lo;
+              }
+            }
+          };
+          if (it & 1) put(best[2 + q]);
+          else put(best[q]);
+        }
+      }
+    }
+  }
+  if (!wave_on) return;
+  // the r-th best of the 64 kept keys of the query block (this lane's 32 and its partner's)
+  const int ntot = nsamp + __shfl_xor(nsamp, 32);
+  const int ncand = P.N - P.bk * P.kept_cnt[row];
+  uint32_t seed = 0u;
+  if (row_ok && ncand > 0) {
+    const long want = (static_cast<long>(SAMPLE_MARGIN) * P.extra * ntot + ncand - 1) / ncand;
+    const int r = static_cast<int>(min(static_cast<long>(8 * SAMPLE_KEEP), max(1l, want)));
+    uint32_t other[4][SAMPLE_KEEP];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < SAMPLE_KEEP; ++e)
+        other[q][e] = static_cast<uint32_t>(__shfl_xor(static_cast<int>(best[q][e]), 32));
+#pragma unroll 1
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < SAMPLE_KEEP; ++e) {
+        const uint32_t v = q == 0 ? best[0][e] : q == 1 ? best[1][e] : q == 2 ? best[2][e] : best[3][e];
+        int cge = 0;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2)
+#pragma unroll
+          for (int e2 = 0; e2 < SAMPLE_KEEP; ++e2)
+            cge += (best[q2][e2] >= v ? 1 : 0) + (other[q2][e2] >= v ? 1 : 0);
+        if (cge >= r) seed = max(seed, v);
+      }
+  }
+  seed = max(seed, static_cast<uint32_t>(__shfl_xor(static_cast<int>(seed), 32)));
+  if (l < 32 && i < P.Mq) P.extra_seed[row] = seed;
+}
+
+// The threshold key thr as a float: a score c passes (float_key(c) >= thr) exactly when
+// c >= key_threshold(thr), for every score that is not NaN (thr = 0 lets every such score pass;
+// NaN scores, which only non-finite inputs produce, never become candidates).
+__device__ __forceinline__ float key_threshold(uint32_t thr) {
+  return thr == 0u ? -__builtin_inff() : key_float(thr);
+}
+
+// repair = 0: every sparse query block from its seed; repair = 1: only the query blocks the
+// merge flagged, from the lowest threshold (every candidate competes: the exact selection).
+template <int D>
+__global__ __launch_bounds__(256, 2) void extra_tile_kernel(Problem P, int repair) {
+  __shared__ ExtraSmem<D> sm;
+  using TT = ExtraTiles<D>;
+  const int E = P.extra, N = P.N, S = P.extra_slices, nl = P.extra_lists;
+  int unit, grp;                                 // unit = (head, slice)
+  if (!xcd_unit(P.B * P.H * S, (P.Mq + EXTRA_GROUP_BF16 - 1) / EXTRA_GROUP_BF16, &unit, &grp)) return;
+  const int bh = unit / S, slice = unit % S, tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int rl = l % 32, i0w = grp * EXTRA_GROUP_BF16 + 32 * w, i = i0w + rl;
+  const int b = bh / P.H, h = bh % P.H;
+  const size_t row = (size_t)bh * P.Mq + (i < P.Mq ? i : 0);
+  bool row_ok = i < P.Mq && !(i >= P.dense_q0 && i < P.dense_q1);
+  if (repair) {
+    row_ok = row_ok && P.extra_flag[row] != 0;
+    if (tid == 0) sm.any = 0;
+    __syncthreads();
+    if (row_ok) sm.any = 1;
+    __syncthreads();
+    if (!sm.any) return;
+  }
+  const uint16_t* kbase = static_cast<const uint16_t*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)h * P.k.sh;
+  const int ts = (((N + S - 1) / S) + 127) / 128 * 128;       // tokens per slice
+  const int t_lo = min(N, slice * ts), t_hi = min(N, t_lo + ts);
+  const int ntile = (t_hi - t_lo + XTOK - 1) / XTOK;           // N is a whole number of tiles
+  TT T;
+  T.init(P, row, i < P.Mq);
+  uint32_t thr = (!repair && row_ok) ? P.extra_seed[row] : 0u;
+  float tf = key_threshold(thr);
+  const bool wave_on = __ballot(row_ok) != 0;
+
+  // key copies: per tile one resource over its 64 rows (scalar arithmetic only); each lane's
+  // offsets inside it are fixed
+  const uint32_t ksn_b = T.ksn_b;
+  uint32_t kvoff[TT::PT];
+#pragma unroll
+  for (int u = 0; u < TT::PT; ++u) {
+    const int s = (u * 4 + w) * 64 + l, r = s / TT::KCH, c = s % TT::KCH;
+    kvoff[u] = static_cast<uint32_t>(r) * ksn_b + kswz<D>(r, c) * 16;
+  }
+  // flag copies: the dword of the lane's kept-bitmap row that holds the tile's key block
+  const uint32_t nwb = static_cast<uint32_t>(P.Mpad / 64) * 8u;
+  const __amdgpu_buffer_rsrc_t frs =
+      make_rsrc(P.kept_bm + (size_t)bh * P.Mq * (P.Mpad / 64), static_cast<uint32_t>(P.Mq) * nwb);
+  const uint32_t fvoff = static_cast<uint32_t>(i < P.Mq ? i : P.Mq) * nwb;
+  constexpr int OPS = TT::PT + 1;          // copies per thread per tile: keys, one flag dword
+  auto issue = [&](int it) {
+    const int t0 = t_lo + it * XTOK;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + (int64_t)t0 * P.k.sn, 64u * ksn_b);
+    char* kd = reinterpret_cast<char*>(sm.k[it % XNB]);
+#pragma unroll
+    for (int u = 0; u < TT::PT; ++u) buf_to_lds16(krs, kvoff[u], kd + (u * 4 + w) * 1024);
+    buf_to_lds4s(frs, fvoff, static_cast<uint32_t>(t0 >> 11) * 4u, sm.fl[it % XNB][0] + 64 * w);
+  };
+
+  // candidate stores go through a buffer resource over this wave's lists of the slice
+  const uint32_t row_stride = (uint32_t)nl * EXTRA_CAP * 8u;          // bytes between query blocks
+  const int nvalid = uniform(max(1, min(32, P.Mq - i0w)));
+  const __amdgpu_buffer_rsrc_t brsrc =
+      make_rsrc(P.extra_buf + ((size_t)bh * P.Mq + uniform(min(i0w, P.Mq - 1))) * nl * EXTRA_CAP +
+                    (size_t)slice * EXTRA_CAP,
+                (uint32_t)(nvalid - 1) * row_stride + EXTRA_CAP * 8u);
+  const uint32_t my_off = (uint32_t)rl * row_stride;
+  int cnt = 0;
+
+  // Append the candidates (bits) of one 32-token step starting at token tw (scores c): lane l
+  // first, then its partner l+32, each in register order; then cut the lists that the next
+  // step could overflow.
+  auto append = [&](const f32x16_t& c, uint32_t bits, int tw) {
+    if (__ballot(bits != 0) == 0) return;
+    const int mine = __popc(bits);
+    const int other = __shfl_xor(mine, 32);
+    uint32_t addr = my_off + static_cast<uint32_t>(cnt + (l < 32 ? 0 : other)) * 8u;
+    cnt += mine + other;
+    const uint32_t tk0 = static_cast<uint32_t>(tw + (l / 32) * 4);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t bit = (bits >> r) & 1u;
+      if (bit) {
+        u32x2 v2;
+        v2.x = __float_as_uint(c[r]);
+        v2.y = tk0 + static_cast<uint32_t>((r / 4) * 8 + (r % 4));
+        __builtin_amdgcn_raw_buffer_store_b64(v2, brsrc, addr, 0, 0);
+      }
+      addr += bit << 3;
+    }
+    uint64_t m = __ballot(l < 32 && cnt > EXTRA_CAP - XSTEP);
+    if (m) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this wave's stores, visible
+      while (m) {
+        const int rr = __builtin_ctzll(m);
+        m &= m - 1;
+        uint2* rb = P.extra_buf + (((size_t)bh * P.Mq + i0w + rr) * nl + slice) * EXTRA_CAP;
+        const int crr = __shfl(cnt, rr);
+        const uint32_t kth = wave_cut(rb, crr, E, sm.hist[w], sm.scr[w]);
+        if (rl == rr) {
+          thr = max(thr, kth);
+          tf = key_threshold(thr);
+          cnt = E;
+        }
+        wave_sync();
+      }
+    }
+  };
+  auto cand_bits = [&](const f32x16_t& c) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int r = 15; r >= 0; --r) bits = bits * 2u + (c[r] >= tf ? 1u : 0u);
+    return bits;
+  };
+
+  for (int it = 0; it < XNB - 1 && it < ntile; ++it) issue(it);
+  // the previous tile's scores and candidate bits, stored one tile late
+  f32x16_t pc0 = {}, pc1 = {};
+  uint32_t pb0 = 0, pb1 = 0;
+  int ptw = 0;
+#pragma unroll 1
+  for (int it = 0; it < ntile; ++it) {
+    const int t0 = t_lo + it * XTOK, j = t0 >> 6;
+    wait_tiles<OPS>(min(XNB - 2, ntile - 1 - it));
+    tile_barrier();
+    const bool cand = row_ok && j < P.M && !FlagCopy::kept(sm.fl[it % XNB][0], j);
+    // every wave has read this tile's flags before its buffer is refilled (a tile later)
+    if (it + XNB - 1 < ntile) issue(it + XNB - 1);
+    append(pc0, pb0, ptw);
+    append(pc1, pb1, ptw + 32);
+    pb0 = pb1 = 0;
+    if (wave_on && __ballot(cand) != 0) {
+      pc0 = T.scores(sm.k[it % XNB], 0);
+      pc1 = T.scores(sm.k[it % XNB], 1);
+      if (cand) {
+        pb0 = cand_bits(pc0);
+        pb1 = cand_bits(pc1);
+      }
+      ptw = t0;
+    }
+  }
+  append(pc0, pb0, ptw);
+  append(pc1, pb1, ptw + 32);
+  // publish the list lengths (in the repair pass only for the flagged query blocks)
+  if (l < 32 && i < P.Mq && (!repair || row_ok)) P.extra_part[row * nl + slice] = cnt;
+}
+
 // Pass 2: best E of the 4*S partial lists of one query block, ranked by token.  The lists stay
 // in memory (L2-resident) and every pass reads them as one flat range with 8 loads in flight
 // per lane.  Radix selection starts below the bits that all keys share (scores of one query
@@ -496,9 +857,9 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) 
   __shared__ int toks[MAX_EXTRA];
   const int i = blockIdx.x, bh = blockIdx.y, l = threadIdx.x;
   const size_t row = (size_t)bh * P.Mq + i;
-  const int E = P.extra, S = P.extra_slices;
+  const int E = P.extra;
   if (i >= P.dense_q0 && i < P.dense_q1) return;          // dense rows keep extra_cnt = 0
-  const int nl = 4 * S;
+  const int nl = P.extra_lists;
   const int* part = P.extra_part + row * nl;
   const uint2* lists = P.extra_buf + row * nl * EXTRA_CAP;
   if (repair == 2) {                                       // exact selection for every row
@@ -661,14 +1022,21 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) 
 
 hipError_t launch_extra_select(const Problem& P, hipStream_t stream) {
   dim3 grid((P.Mq + XR - 1) / XR, P.B * P.H, P.extra_slices);
+  const int ngrp = (P.Mq + EXTRA_GROUP_BF16 - 1) / EXTRA_GROUP_BF16;
+  dim3 g16(xcd_grid(P.B * P.H * P.extra_slices, ngrp));
+  dim3 gseed(xcd_grid(P.B * P.H, ngrp));
   dim3 g2(P.Mq, P.B * P.H);
   auto pass1 = [&](int repair) {
     if (P.dtype == 0) {
-      if (P.d == 128) hipLaunchKernelGGL((extra_select_kernel<uint16_t, 128>), grid, dim3(256), 0, stream, P, repair);
-      else hipLaunchKernelGGL((extra_select_kernel<uint16_t, 64>), grid, dim3(256), 0, stream, P, repair);
+      if (!repair) {
+        if (P.d == 128) hipLaunchKernelGGL(extra_seed_kernel<128>, gseed, dim3(256), 0, stream, P);
+        else hipLaunchKernelGGL(extra_seed_kernel<64>, gseed, dim3(256), 0, stream, P);
+      }
+      if (P.d == 128) hipLaunchKernelGGL(extra_tile_kernel<128>, g16, dim3(256), 0, stream, P, repair);
+      else hipLaunchKernelGGL(extra_tile_kernel<64>, g16, dim3(256), 0, stream, P, repair);
     } else {
-      if (P.d == 128) hipLaunchKernelGGL((extra_select_kernel<float, 128>), grid, dim3(256), 0, stream, P, repair);
-      else hipLaunchKernelGGL((extra_select_kernel<float, 64>), grid, dim3(256), 0, stream, P, repair);
+      if (P.d == 128) hipLaunchKernelGGL(extra_select_kernel<128>, grid, dim3(256), 0, stream, P, repair);
+      else hipLaunchKernelGGL(extra_select_kernel<64>, grid, dim3(256), 0, stream, P, repair);
     }
     return hipGetLastError();
   };

@@ -31,29 +31,8 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 // ------------------------------------------------------------------ bf16 path
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Asynchronous 16-byte global -> LDS copy through a buffer resource: lane l's 16 bytes land at
-// `wave_dst` + 16*l (the same `wave_dst` for the whole wave); `voff` is the lane's byte offset
-// from the resource base.  Out-of-range offsets read zero.
-__device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* wave_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(wave_dst), 16, voff, 0, 0, 0);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// LDS swizzles: the 16-byte chunk c of row r is stored at chunk position kswz/vswz(r, c), so that
-// any 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte bank groups.
-template <int D>
-__device__ __forceinline__ int kswz(int r, int c) {
-  if constexpr (D == 128) return c ^ (r & 15);        // 256-byte rows
-  else return c ^ ((r >> 1) & 7);                     // 128-byte rows
-}
-__device__ __forceinline__ int vswz(int r, int c) { return c ^ ((r >> 1) & 7); }   // 128-byte rows
+// LDS swizzle of the transposed V rows (128 bytes: 64 keys), as kswz for the key rows.
+__device__ __forceinline__ int vswz(int r, int c) { return c ^ ((r >> 1) & 7); }
 // E4M3 key rows (fp8-QK): D bytes, D/16 chunks
 template <int D>
 __device__ __forceinline__ int kswz8(int r, int c) { return c ^ ((r >> 1) & (D / 16 - 1)); }

@@ -218,8 +218,12 @@ int local3d_check_args(const void* q, const void* k, const void* v, void* out,
  *   extra_cnt int32 [B*H, Mq]      number of extra tokens
  *   extra_idx int32 [B*H, Mq, 256] extra token indices, ascending, first extra_cnt valid
  *   extra_buf, extra_part: scratch of the extra-token selection (candidate lists per query
- *             block, token slice and wave, and their lengths); extra_buf also holds the
- *             partial sums of the per-call counters when they are requested
+ *             block: one per token slice for 16-bit tensors, one per slice and wave for fp32;
+ *             and their lengths); extra_buf also holds the partial sums of the per-call
+ *             counters when they are requested
+ *   extra_seed uint32 [B*H, Mq]    scratch of the extra-token selection (16-bit tensors): the
+ *             threshold each query block's first pass starts from, seeded from a sample of
+ *             the keys, as an order-preserving key of the fp32 score
  *   extra_flag int32 [B*H, Mq]     1 where the extra-token selection's first pass, whose
  *             threshold is seeded from a sample of the keys, kept fewer candidates than the
  *             selection needs, so that the query block was selected again with every
@@ -245,6 +249,7 @@ typedef struct solattn_ws_layout {
   size_t k8, kb8;                /* SOLATTN_BF16_FP8QK only: E4M3 key and pooled-key tiles  */
   size_t pair_plan;              /* 16-bit types with block_q 64 only (else 0): int64
                                     [B*H, 8], see above                                      */
+  size_t extra_seed;             /* uint32 [B*H, Mq]: seeded threshold keys, see above       */
 } solattn_ws_layout;
 
 /* Fills *layout for a call of this shape.  Returns SOLATTN_OK or SOLATTN_EINVAL. */
