@@ -130,17 +130,36 @@ __host__ __device__ inline void flash_unit_blocks(int G, int Mq, int dq0, int dq
 constexpr int EXTRA_GROUP_BF16 = 128;
 constexpr int EXTRA_GROUP_F32 = 32;
 
-// Token slices of the extra-token selection and candidate lists per query block.  16-bit: enough
-// slices for about 2048 workgroups (at most 16), one list per slice; fp32: enough for 1536 (at
-// most 4), one list per slice and wave.
+// Token slices of the extra-token selection and candidate lists per query block.  fp32: enough
+// slices for about 1536 workgroups (at most 4), one list per slice and wave.  16-bit: the slice
+// count (at most 16) whose workgroups fill the last of their rounds best (EXTRA_SLOTS resident
+// at a time: two per compute unit of the 256), preferring fewer slices on near ties; one list per
+// slice.
+constexpr int EXTRA_SLOTS = 512;
 __host__ __device__ inline void extra_split(bool f32, int B, int H, int Mq, int* slices, int* lists) {
-  const int grp = f32 ? EXTRA_GROUP_F32 : EXTRA_GROUP_BF16;
-  const long groups = (long)((Mq + grp - 1) / grp) * B * H;
-  const long want = f32 ? 1536 : 2048, cap = f32 ? 4 : 16;
-  long s = (want + groups - 1) / groups;
-  s = s < 1 ? 1 : (s > cap ? cap : s);
-  *slices = (int)s;
-  *lists = f32 ? 4 * (int)s : (int)s;
+  if (f32) {
+    const long groups = (long)((Mq + EXTRA_GROUP_F32 - 1) / EXTRA_GROUP_F32) * B * H;
+    long s = (1536 + groups - 1) / groups;
+    s = s < 1 ? 1 : (s > 4 ? 4 : s);
+    *slices = (int)s;
+    *lists = 4 * (int)s;
+    return;
+  }
+  const long groups = (long)((Mq + EXTRA_GROUP_BF16 - 1) / EXTRA_GROUP_BF16) * B * H;
+  int best = 1;
+  double best_eff = -1.0;
+  for (int s = 1; s <= 16; ++s) {
+    const long wg = groups * s;
+    const long rounds = (wg + EXTRA_SLOTS - 1) / EXTRA_SLOTS;
+    // a fill of one round or less leaves the chip idle; count it by its share of the slots
+    const double eff = (double)wg / (double)(rounds * EXTRA_SLOTS);
+    if (eff > best_eff + 0.02) {
+      best_eff = eff;
+      best = s;
+    }
+  }
+  *slices = best;
+  *lists = best;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

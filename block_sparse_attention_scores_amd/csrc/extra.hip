@@ -196,7 +196,7 @@ __device__ uint32_t wave_cut(uint2* buf, int cnt, int E, int* hist, int* scratch
 // expected at or above it (r at most the 64 kept scores).
 constexpr int SAMPLE_STEPS = 64;
 constexpr int SAMPLE_KEEP = 8;
-constexpr int SAMPLE_MARGIN = 6;
+constexpr int SAMPLE_MARGIN = 4;
 
 __device__ __forceinline__ int sample_run(int s, int nsteps, int M) {
   const int span = max(1, M / nsteps);
