@@ -13,8 +13,8 @@
 //   table, and sink_conditioning row).  Query blocks in the dense row range keep every block.
 // The kept set is written twice: as an ascending index list and as a bitmap (bit j of word
 // j/64), which the attention kernel walks without touching memory.
-// One 256-thread workgroup per row; all reductions have a fixed order, so results are
-// deterministic.  Also writes each block's centroid multiplicity (0 = attended exactly).
+// One wave per row (four rows per workgroup); all reductions have a fixed order, so results
+// are deterministic.  Also writes each block's centroid multiplicity (0 = attended exactly).
 #include "common.h"
 #include "launch.h"
 
@@ -26,41 +26,30 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Sum over the 256 threads, identical result on every thread.
-__device__ float block_sum(float v, float* sh) {
-  v = wave_sum(v);
-  const int w = threadIdx.x / 64;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[w] = v;
-  __syncthreads();
-  return ((sh[0] + sh[1]) + sh[2]) + sh[3];
+// Orders this wave's LDS accesses before and after it (the waves of a workgroup work on
+// different rows and never share LDS here).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
-// Inclusive prefix sum over the 256 threads (thread order).  *total gets the sum.
-__device__ int block_scan_incl(int v, int* sh, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x / 64;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  __syncthreads();
-  if (lane == 63) sh[w] = v;
-  __syncthreads();
-  int before = 0;
-  for (int u = 0; u < w; ++u) before += sh[u];
-  *total = sh[0] + sh[1] + sh[2] + sh[3];
-  return v + before;
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
 }
+
+// One wave per row, SEL_ROWS rows per workgroup; no workgroup barrier, every reduction is a
+// fixed-order wave reduction (deterministic).
+constexpr int SEL_ROWS = 4;
 
 __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
-  extern __shared__ uint32_t nbm[];   // local 3-D mode: neighbourhood bitmap, Mpad/32 words
-  __shared__ float fsh[4];
-  __shared__ int ish[4];
-  __shared__ int hist[256];
-  __shared__ int pick[2];
+  extern __shared__ uint32_t nbm_all[];   // local 3-D mode: one neighbourhood bitmap (Mpad/32 words) per wave
+  __shared__ int hist_all[SEL_ROWS][256];
 
-  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = blockIdx.x * SEL_ROWS + wv, bh = blockIdx.y;
+  if (i >= P.Mq) return;                   // the whole wave: nothing below waits for other waves
   const int M = P.M;
   const size_t row = (size_t)bh * P.Mq + i;
   const float* s = P.scores + row * M;
@@ -68,22 +57,21 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
   uint8_t* mult = P.mult + row * P.Mpad;
   float* cb = P.cbias + row * P.Mpad;
   uint64_t* bm = P.kept_bm + row * (P.Mpad / 64);
-  const int lane = tid & 63, wv = tid >> 6;
   // centroid logit offset in raw-score units: ln(block size) / scale
   const float log2_bk = __logf(static_cast<float>(P.bk)) / P.scale;
 
   const bool dense = i >= P.dense_q0 && i < P.dense_q1;
   if (dense || (P.mode == 0 && P.keep_all)) {
-    for (int j = tid; j < P.Mpad; j += 256) {
+    for (int j = lane; j < P.Mpad; j += 64) {
       if (j < M) kidx[j] = j;
       mult[j] = 0;
       cb[j] = -__builtin_inff();
     }
-    for (int wd = tid; wd < P.Mpad / 64; wd += 256) {
+    for (int wd = lane; wd < P.Mpad / 64; wd += 64) {
       const int nb = M - 64 * wd;       // blocks of this word that exist
       bm[wd] = nb >= 64 ? ~0ull : ((1ull << nb) - 1ull);
     }
-    if (tid == 0) {
+    if (lane == 0) {
       P.kept_cnt[row] = M;
       P.extra_cnt[row] = 0;
     }
@@ -100,26 +88,27 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
   uint32_t kstar = 0;         // sla: key of the k-th largest non-forced score
   int need_eq = 0;            // sla: how many scores equal to kstar to take (lowest index first)
   bool sla_any = false;
+  uint32_t* nbm = nbm_all + (size_t)wv * (P.Mpad / 32);
 
   if (P.mode == 0) {
     float acc = 0.f;
-    for (int j = tid; j < M; j += 256) acc += s[j];
-    const float mu = block_sum(acc, fsh) / static_cast<float>(M);
+    for (int j = lane; j < M; j += 64) acc += s[j];
+    const float mu = wave_sum(acc) / static_cast<float>(M);
     float acc2 = 0.f;
-    for (int j = tid; j < M; j += 256) {
+    for (int j = lane; j < M; j += 64) {
       const float dv = s[j] - mu;
       acc2 = fmaf(dv, dv, acc2);
     }
-    const float var = block_sum(acc2, fsh) / static_cast<float>(M);
+    const float var = wave_sum(acc2) / static_cast<float>(M);
     const float sd = sqrtf(var);
     theta = sd > 0.f ? fmaf(P.tau, sd, mu) : mu;
   } else if (P.mode == 2) {
-    // one thread per query token: mark the blocks of the token and of its grid neighbours
-    for (int wd = tid; wd < P.Mpad / 32; wd += 256) nbm[wd] = 0u;
-    __syncthreads();
-    if (tid < P.bq) {
-      const int hw = P.height * P.width;
-      const int p = gi * P.bq + tid;
+    // one lane per query token: mark the blocks of the token and of its grid neighbours
+    for (int wd = lane; wd < P.Mpad / 32; wd += 64) nbm[wd] = 0u;
+    wave_lds_sync();
+    const int hw = P.height * P.width;
+    for (int q = lane; q < P.bq; q += 64) {
+      const int p = gi * P.bq + q;
       const int t = p / hw, r = p - t * hw;
       const int y = r / P.width, x = r - y * P.width;
       auto mark = [&](int tok) {
@@ -134,48 +123,66 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
       if (x > 0) mark(p - 1);
       if (x + 1 < P.width) mark(p + 1);
     }
-    __syncthreads();
+    wave_lds_sync();
   } else {
     const int nforced = min(P.sink_blocks, M) + (diag_hi - diag_lo + 1) -
                         max(0, min(diag_hi, P.sink_blocks - 1) - diag_lo + 1);
     int need = min(M - nforced, P.k_sla);
     sla_any = need > 0;
     if (sla_any) {
+      int* hist = hist_all[wv];
       uint32_t prefix = 0, pmask = 0;
       for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        hist[tid] = 0;
-        __syncthreads();
-        for (int j = tid; j < M; j += 256) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
+        wave_lds_sync();
+        for (int j = lane; j < M; j += 64) {
           if (forced(j)) continue;
           const uint32_t key = float_key(s[j]);
           if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
         }
-        __syncthreads();
-        // thread t looks at digit 255-t; counts accumulate from the top digit down
-        const int c = hist[255 - tid];
-        int total;
-        const int incl = block_scan_incl(c, ish, &total);
-        const int excl = incl - c;
-        if (excl < need && need <= incl) {
-          pick[0] = 255 - tid;
-          pick[1] = excl;
+        wave_lds_sync();
+        // lane l holds digits 255-4l .. 252-4l; counts accumulate from the top digit down
+        int c[4], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c[q] = hist[255 - 4 * lane - q];
+          sum += c[q];
         }
-        __syncthreads();
-        prefix |= static_cast<uint32_t>(pick[0]) << shift;
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t = __shfl_up(incl, o);
+          if (lane >= o) incl += t;
+        }
+        int ex = incl - sum, dig = -1, above = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (dig < 0 && ex < need && need <= ex + c[q]) {
+            dig = 255 - 4 * lane - q;
+            above = ex;
+          }
+          ex += c[q];
+        }
+        const uint64_t hit = __ballot(dig >= 0);     // exactly one lane
+        const int src = static_cast<int>(__builtin_ctzll(hit));
+        dig = __builtin_amdgcn_readlane(dig, src);
+        above = __builtin_amdgcn_readlane(above, src);
+        prefix |= static_cast<uint32_t>(dig) << shift;
         pmask |= 0xFFu << shift;
-        need -= pick[1];
-        __syncthreads();
+        need -= above;
+        wave_lds_sync();                               // the histogram is cleared next pass
       }
       kstar = prefix;
       need_eq = need;
     }
   }
 
-  // ordered compaction of the kept blocks
+  // ordered compaction of the kept blocks, 64 at a time: the keep ballot is the bitmap word
   int base = 0, eq_base = 0;
-  for (int j0 = 0; j0 < M; j0 += 256) {
-    const int j = j0 + tid;
+  for (int j0 = 0; j0 < M; j0 += 64) {
+    const int j = j0 + lane;
     bool keep = false, eq = false;
     if (j < M) {
       if (forced(j)) {
@@ -190,27 +197,24 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
         eq = key == kstar;
       }
     }
-    int tot_eq;
-    const int eq_rank = block_scan_incl(eq ? 1 : 0, ish, &tot_eq) - (eq ? 1 : 0) + eq_base;
-    if (eq && eq_rank < need_eq) keep = true;
-    eq_base += tot_eq;
-    int tot;
-    const int pos = block_scan_incl(keep ? 1 : 0, ish, &tot) - (keep ? 1 : 0) + base;
-    if (keep) kidx[pos] = j;
+    const uint64_t eqm = __ballot(eq);
+    if (eq && eq_base + lanes_below(eqm) < need_eq) keep = true;
+    eq_base += __popcll(eqm);
     const uint64_t word = __ballot(keep);
-    const int wd = (j0 >> 6) + wv;
-    if (lane == 0 && wd < P.Mpad / 64) bm[wd] = word;
+    if (keep) kidx[base + lanes_below(word)] = j;
+    if (lane == 0) bm[j0 >> 6] = word;
     if (j < M) {
       mult[j] = keep ? 0 : static_cast<uint8_t>(P.bk);
       cb[j] = keep ? -__builtin_inff() : log2_bk;
     }
-    base += tot;
+    base += __popcll(word);
   }
-  for (int j = M + tid; j < P.Mpad; j += 256) {
+  for (int wd = ((M + 63) >> 6) + lane; wd < P.Mpad / 64; wd += 64) bm[wd] = 0ull;
+  for (int j = M + lane; j < P.Mpad; j += 64) {
     mult[j] = 0;
     cb[j] = -__builtin_inff();
   }
-  if (tid == 0) {
+  if (lane == 0) {
     P.kept_cnt[row] = base;
     P.extra_cnt[row] = 0;
   }
@@ -253,8 +257,8 @@ hipError_t launch_pair_plan(const Problem& P, hipStream_t stream) {
 }
 
 hipError_t launch_block_select(const Problem& P, hipStream_t stream) {
-  dim3 grid(P.Mq, P.B * P.H);
-  const size_t lds = P.mode == 2 ? (size_t)(P.Mpad / 32) * 4 : 0;
+  dim3 grid((P.Mq + SEL_ROWS - 1) / SEL_ROWS, P.B * P.H);
+  const size_t lds = P.mode == 2 ? (size_t)SEL_ROWS * (P.Mpad / 32) * 4 : 0;
   hipLaunchKernelGGL(block_select_kernel, grid, dim3(256), lds, stream, P);
   return hipGetLastError();
 }
