@@ -4,70 +4,85 @@
 //
 // fp32 throughout: the selection compares scores against mean + tau*std of the row, and a
 // bf16 rounding of the pooled vectors would move scores far more than the 1e-4*std band the
-// masks are checked to.  A 64x64 output tile per workgroup, d staged through LDS in slices
-// of 32; every output is one sequential fp32 FMA chain over d.
+// masks are checked to.  The products run on the fp32 matrix instruction (32x32x2: exact fp32
+// products, fp32 accumulation): a 128x128 output tile per workgroup, each wave 64x64 as four
+// 32x32 accumulators; q̄ and k̄ rows are staged through LDS in slices of 32 dimensions.
 #include "common.h"
 #include "launch.h"
 
 namespace solattn {
 
+typedef float f32x16_s __attribute__((ext_vector_type(16)));
+
 template <int D>
 __global__ __launch_bounds__(256) void block_score_kernel(Problem P) {
-  constexpr int DS = 32;
-  __shared__ float As[DS][64 + 4];
-  __shared__ float Bs[DS][64 + 4];
+  constexpr int DC = 32;                       // dimensions per LDS slice
+  constexpr int LD = DC + 1;                   // padded row: 32 rows read at one column hit distinct banks
+  __shared__ float As[128 * LD];
+  __shared__ float Bs[128 * LD];
   const int bh = blockIdx.z;
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  const int i0 = blockIdx.y * 128, j0 = blockIdx.x * 128;
+  const int tid = threadIdx.x, l = tid % 64, w = tid / 64;
+  const int c32 = l % 32, h = l / 32;
+  const int wi = 64 * (w / 2), wj = 64 * (w % 2);   // this wave's 64x64 sub-tile
   const float* qb = P.qbar + (size_t)bh * P.Mq * D;
   const float* kb = P.kbar + (size_t)bh * P.M * D;
 
-  float acc[4][4];
+  f32x16_s acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16_s{};
 
-  for (int d0 = 0; d0 < D; d0 += DS) {
+  for (int d0 = 0; d0 < D; d0 += DC) {
     __syncthreads();
+    // 128 rows x 32 floats of each operand: 1024 float4 per operand, four per thread
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const int idx = tid + 256 * u, r = idx / 8, c4 = idx % 8;
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
       if (i0 + r < P.Mq) x = *reinterpret_cast<const float4*>(qb + (size_t)(i0 + r) * D + d0 + 4 * c4);
       if (j0 + r < P.M) y = *reinterpret_cast<const float4*>(kb + (size_t)(j0 + r) * D + d0 + 4 * c4);
-      As[4 * c4 + 0][r] = x.x; As[4 * c4 + 1][r] = x.y; As[4 * c4 + 2][r] = x.z; As[4 * c4 + 3][r] = x.w;
-      Bs[4 * c4 + 0][r] = y.x; Bs[4 * c4 + 1][r] = y.y; Bs[4 * c4 + 2][r] = y.z; Bs[4 * c4 + 3][r] = y.w;
+      float* a = As + r * LD + 4 * c4;
+      float* b = Bs + r * LD + 4 * c4;
+      a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
+      b[0] = y.x; b[1] = y.y; b[2] = y.z; b[3] = y.w;
     }
     __syncthreads();
-#pragma unroll 8
-    for (int e = 0; e < DS; ++e) {
-      float av[4], bv[4];
+    // step kk: lanes 0-31 supply dimension 2kk, lanes 32-63 dimension 2kk+1 (A row / B column c32)
+#pragma unroll 4
+    for (int kk = 0; kk < DC / 2; ++kk) {
+      const int k = 2 * kk + h;
+      float av[2], bv[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = As[e][ty + 16 * a];
+      for (int t = 0; t < 2; ++t) {
+        av[t] = As[(wi + 32 * t + c32) * LD + k];
+        bv[t] = Bs[(wj + 32 * t + c32) * LD + k];
+      }
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = Bs[e][tx + 16 * b];
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(av[a], bv[b], acc[a][b]);
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
     }
   }
+  // accumulator register r of tile (a, b): row wi + 32a + (r/4)*8 + 4h + r%4, column wj + 32b + c32
   float* S = P.scores + (size_t)bh * P.Mq * P.M;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ty + 16 * a;
-    if (i >= P.Mq) continue;
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = j0 + tx + 16 * b;
-      if (j < P.M) S[(size_t)i * P.M + j] = acc[a][b] * P.scale;
+    for (int b = 0; b < 2; ++b) {
+      const int j = j0 + wj + 32 * b + c32;
+      if (j >= P.M) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + wi + 32 * a + (r / 4) * 8 + 4 * h + (r % 4);
+        if (i < P.Mq) S[(size_t)i * P.M + j] = acc[a][b][r] * P.scale;
+      }
     }
-  }
 }
 
 hipError_t launch_block_score(const Problem& P, hipStream_t stream) {
-  dim3 grid((P.M + 63) / 64, (P.Mq + 63) / 64, P.B * P.H);
+  dim3 grid((P.M + 127) / 128, (P.Mq + 127) / 128, P.B * P.H);
   if (P.d == 128) hipLaunchKernelGGL(block_score_kernel<128>, grid, dim3(256), 0, stream, P);
   else hipLaunchKernelGGL(block_score_kernel<64>, grid, dim3(256), 0, stream, P);
   return hipGetLastError();
