@@ -980,29 +980,33 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) 
     });
   }
   wave_sync();
-  // survivors are in toks[0..c) in any order: sort them ascending (bitonic network over
-  // MAX_EXTRA slots, padding at the end), write them out, and take them out of their key
-  // blocks' centroid terms (key blocks are 64 tokens: block_k is 64 in this library)
+  // survivors are in toks[0..c): sort them ascending, write them out, and take them out of
+  // their key blocks' centroid terms (key blocks are 64 tokens: block_k is 64 in this library).
+  // In the register paths the survivors keep the order of the lists, which is ascending except
+  // inside one 32-token step (a lane's tokens, then its partner's); an odd-even transposition
+  // sort, run until a whole round swaps nothing, takes a few rounds there (and stays exact for
+  // any order).
   const int c = scr[3];
-  for (int p = c + l; p < MAX_EXTRA; p += 64) toks[p] = 0x7fffffff;
   wave_sync();
 #pragma unroll 1
-  for (int kk = 2; kk <= MAX_EXTRA; kk <<= 1) {
-#pragma unroll 1
-    for (int j = kk >> 1; j > 0; j >>= 1) {
+  for (;;) {
+    bool swapped = false;
 #pragma unroll
-      for (int p = l; p < MAX_EXTRA; p += 64) {
-        const int pj = p ^ j;
-        if (pj > p) {
-          const int x = toks[p], y = toks[pj];
-          if ((x > y) == ((p & kk) == 0)) {
+    for (int ph = 0; ph < 2; ++ph) {
+#pragma unroll
+      for (int p = 2 * l + ph; p < MAX_EXTRA; p += 128) {
+        if (p + 1 < c) {
+          const int x = toks[p], y = toks[p + 1];
+          if (x > y) {
             toks[p] = y;
-            toks[pj] = x;
+            toks[p + 1] = x;
+            swapped = true;
           }
         }
       }
       wave_sync();
     }
+    if (__ballot(swapped) == 0) break;
   }
   int* out = P.extra_idx + row * MAX_EXTRA;
   uint8_t* mr = P.mult + row * P.Mpad;
