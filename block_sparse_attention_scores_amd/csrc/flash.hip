@@ -47,6 +47,7 @@ struct FlashSmem {
   __attribute__((aligned(16))) float bias[2][2][64];
   __attribute__((aligned(16))) float zero[64];   // the bias of plain key tiles
   __attribute__((aligned(16))) uint8_t ke[2][QK8 ? 64 : 16];   // E4M3 scale codes of the K rows
+  __attribute__((aligned(16))) int eidx[2][MAX_EXTRA];         // extra-token lists of the pair
 };
 
 struct TileDesc {
@@ -438,6 +439,10 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
   };
 
   if (tid < 64) sm.zero[tid] = 0.f;       // visible after the first barrier of the loop
+  // the pair's extra-token lists go to LDS now (wave g copies block g's, 16 bytes a lane) and
+  // arrive with the first tile, so the gather after the main loop reads its indices from LDS
+  if (w < G && ne[w] > 0)
+    buf_to_lds16(make_rsrc(elist[w], MAX_EXTRA * 4), static_cast<uint32_t>(l) * 16u, sm.eidx[w]);
   TileDesc cur = it.next();
   int bf = 0;
   issue(cur, 0);
@@ -461,7 +466,7 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
 #pragma unroll 1
   for (int gg = 0; gg < G; ++gg) {
     const int cnt = ne[gg];
-    const int* el = elist[gg];
+    const int* el = sm.eidx[gg];
 #pragma unroll 1
     for (int e0 = 0; e0 < cnt; e0 += 64) {
       __syncthreads();
