@@ -204,6 +204,19 @@ __device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(wave_dst), 16, voff, 0, 0, 0);
 }
 
+// The same with a wave-uniform byte offset `soff` added to every lane's.
+__device__ __forceinline__ void buf_to_lds16s(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                              void* wave_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(wave_dst), 16, voff, soff, 0, 0);
+}
+
+// Asynchronous 16-byte global -> LDS gather: each lane names its own source address; lane l's
+// 16 bytes land at `wave_dst` + 16*l.
+typedef __attribute__((address_space(1))) void global_void_t;
+__device__ __forceinline__ void glb_to_lds16(const void* src, void* wave_dst) {
+  __builtin_amdgcn_global_load_lds((global_void_t*)(const_cast<void*>(src)), (lds_void_t*)(wave_dst), 16, 0, 0);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }

@@ -2,17 +2,19 @@
 // softmax (star7 README, "Sol": kept K/V blocks exactly, skipped blocks through their
 // centroids, merged in one FP32 online softmax; "SLA": only the routed blocks):
 //   1. the kept key blocks (for dense query blocks: every block),
-//   2. the extra tokens, gathered 64 at a time,
-//   3. sol only: the centroid terms of every key block, 64 per tile, each with logit
+//   2. sol only: the centroid terms of every key block, 64 per tile, each with logit
 //      q.k̄_j / sqrt(d) + ln(m_ij) (m_ij = tokens of block j not attended exactly; a kept
-//      block has m = 0 and drops out).
-// Every tile is the same computation on a 64-key K tile and a transposed V tile in LDS with a
-// per-key additive bias, so one inner loop serves all three phases.
+//      block has m = 0 and drops out),
+//   3. the extra tokens, gathered 64 at a time.
+// Every tile is the same computation on a 64-key K tile and a V tile in LDS with a per-key
+// additive bias; tiles stream through double-buffered LDS (phases 1 and 2 in one loop, the
+// extra tokens in a second one).
 //
 // bf16 kernel: each wave owns 32 query rows.  S^T = K Q^T and O^T += V^T P^T run on the
 // 32x32x16 bf16 matrix instruction: the score accumulator's lane layout (lane = query row,
 // 16 registers = keys) feeds P^T straight to the second product, so P never leaves registers;
-// the V tile is stored transposed with a key permutation that matches that layout.  Running
+// the V tile is stored transposed with a key permutation that matches that layout (extra-token
+// tiles, gathered row by row, keep V row-major and read it two bytes at a time).  Running
 // max and sum are fp32 and kept per lane (the two half-waves hold the same query rows and
 // combine their partial sums at the end).  Logits are taken in base 2.
 //
@@ -50,6 +52,11 @@ struct FlashSmem {
   __attribute__((aligned(16))) int eidx[2][MAX_EXTRA];         // extra-token lists of the pair
 };
 
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 struct TileDesc {
   int kind;   // 0 kept key block, 1 extra tokens of one query block, 2 centroids, 3 end
   int idx;    // key block j | first extra position | first centroid index
@@ -62,7 +69,7 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t x, int lane) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// Walks the pipelined work of a pair of query blocks: every key block kept by either of them,
+// Walks the main loop's work of a pair of query blocks: every key block kept by either of them,
 // in ascending order, then the centroid tiles.  The two kept-block bitmaps are held one 64-bit
 // word per lane (lane l: blocks 64l..64l+63), so finding the next tile is a ballot and a few
 // lane reads, with no memory access.  Every decision is uniform across the wave.
@@ -225,31 +232,30 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
     }
   }
 
-  // per-lane byte offsets of the tile loads (slot s of this lane in instruction u):
-  // K row r = s / KCH, chunk c = s % KCH, stored at swizzled chunk kswz(r, c);
-  // transposed V row vr = s / 8, chunk vc = s % 8, stored at vswz(vr, vc).
+  // per-lane byte offsets of the tile loads.  Instruction u of wave w moves 16-byte slot
+  // s = (4u + w) * 64 + l of the tile: K row r = s / KCH, chunk c = s % KCH, stored at swizzled
+  // chunk kswz(r, c); transposed V row vr = s / 8, chunk vc = s % 8, stored at vswz(vr, vc).
+  // Instruction u moves rows KSTEP*u further on, which leaves both swizzles unchanged (they
+  // depend on the row's low 4 bits, and KSTEP is a multiple of 16), so each offset is the lane's
+  // u = 0 offset plus a wave-uniform step.
   const uint32_t ksn_b = static_cast<uint32_t>(P.k.sn) * 2u;
   const uint32_t vsn_b = static_cast<uint32_t>(P.v.sn) * 2u;
-  constexpr int PK = QK8 ? PER_THREAD8 : PER_THREAD;
-  uint32_t krow[PK], kcol[PK], voff[PER_THREAD];
-#pragma unroll
-  for (int u = 0; u < PK; ++u) {
-    const int s = (u * 4 + w) * 64 + l;
-    if constexpr (QK8) {
-      const int r = s / KCH8, c = s % KCH8;
-      krow[u] = r;
-      kcol[u] = kswz8<D>(r, c) * 16;
-    } else {
-      const int r = s / KCH, c = s % KCH;
-      krow[u] = r;
-      kcol[u] = kswz<D>(r, c) * 16;
-    }
+  constexpr int KSTEP = QK8 ? 256 / KCH8 : 256 / KCH;   // K rows per instruction
+  static_assert(KSTEP % 16 == 0, "row step must keep the swizzle");
+  uint32_t krow0, kcol0;
+  if constexpr (QK8) {
+    const int s0 = w * 64 + l, r = s0 / KCH8, c = s0 % KCH8;
+    krow0 = r;
+    kcol0 = kswz8<D>(r, c) * 16;
+  } else {
+    const int s0 = w * 64 + l, r = s0 / KCH, c = s0 % KCH;
+    krow0 = r;
+    kcol0 = kswz<D>(r, c) * 16;
   }
-#pragma unroll
-  for (int u = 0; u < PER_THREAD; ++u) {
-    const int s = (u * 4 + w) * 64 + l;
-    const int vr = s / 8, vc = s % 8;
-    voff[u] = vr * 128 + vswz(vr, vc) * 16;
+  uint32_t voff0;
+  {
+    const int s0 = w * 64 + l, vr = s0 / 8, vc = s0 % 8;
+    voff0 = vr * 128 + vswz(vr, vc) * 16;
   }
 
   // ---- issue the asynchronous loads of one tile into buffer bf
@@ -274,16 +280,16 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
                                           : P.kb8 + ((size_t)bh * (P.Mpad / 64) + t.idx / 64) * TB8;
       const __amdgpu_buffer_rsrc_t kr = make_rsrc(k8base, TB8);
 #pragma unroll
-      for (int u = 0; u < PER_THREAD8; ++u) buf_to_lds16(kr, krow[u] * D + kcol[u], kd + u * 4096);
+      for (int u = 0; u < PER_THREAD8; ++u) buf_to_lds16s(kr, krow0 * D + kcol0, u * KSTEP * D, kd + u * 4096);
       if (w == 0 && l < 4) buf_to_lds16(kr, 64 * D + 16 * l, sm.ke[bf]);   // the rows' scale codes
 #pragma unroll
-      for (int u = 0; u < PER_THREAD; ++u) buf_to_lds16(vr, voff[u], vd + u * 4096);
+      for (int u = 0; u < PER_THREAD; ++u) buf_to_lds16s(vr, voff0, u * 4096, vd + u * 4096);
     } else {
       const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, 64u * krow_b);
 #pragma unroll
       for (int u = 0; u < PER_THREAD; ++u) {
-        buf_to_lds16(kr, krow[u] * krow_b + kcol[u], kd + u * 4096);
-        buf_to_lds16(vr, voff[u], vd + u * 4096);
+        buf_to_lds16s(kr, krow0 * krow_b + kcol0, u * KSTEP * krow_b, kd + u * 4096);
+        buf_to_lds16s(vr, voff0, u * 4096, vd + u * 4096);
       }
     }
     if (t.kind == 2 && w == 0) {
@@ -298,6 +304,25 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
     }
   };
 
+  // ---- extra tokens e0 .. e0+63 of block gg into buffer bf, gathered row by row (rows past
+  // the count repeat the first token and get bias -inf): K rows into the swizzled key layout, V
+  // rows row-major with the 16-byte chunk c of row r at position c ^ (r & 4)
+  auto issue_extra = [&](int gg, int e0, int bf) {
+    char* kd = reinterpret_cast<char*>(sm.k[bf]) + w * 1024;
+    char* vd = reinterpret_cast<char*>(sm.v[bf]) + w * 1024;
+    const int cnt = gg ? ne[1] : ne[0];
+    const uint32_t vcol0 = ((static_cast<uint32_t>(l) % KCH) ^ (krow0 & 4)) << 4;
+#pragma unroll
+    for (int u = 0; u < PER_THREAD; ++u) {
+      const int r = krow0 + KSTEP * u;
+      const int e = e0 + r < cnt ? e0 + r : e0;
+      const size_t tok = static_cast<uint32_t>(sm.eidx[gg][e]);
+      glb_to_lds16(reinterpret_cast<const char*>(Kb) + tok * ksn_b + kcol0, kd + u * 4096);
+      glb_to_lds16(reinterpret_cast<const char*>(Vb) + tok * vsn_b + vcol0, vd + u * 4096);
+    }
+    if (w == 0) sm.bias[bf][gg][l] = e0 + l < cnt ? 0.f : -__builtin_inff();
+  };
+
   f32x16_t o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
@@ -308,6 +333,10 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
   // a lane constant, so each read is one XOR with a compile-time constant.
   const uint32_t ak = c32 * (D * 2) + 16 * (kswz<D>(c32, 0) ^ h32);
   const uint32_t av = c32 * 128 + 16 * (vswz(c32, 0) ^ h32);
+  // row-major V (extra-token tiles): element (key, d) at key * 2D + 16 * ((d / 8) ^ (key & 4)) +
+  // 2 * (d % 8); this lane's keys all have key & 4 = 4 h32
+  const uint32_t rmo = 8 * h32 * D + 16 * (c32 >> 3) + 2 * (c32 & 7);
+  const uint32_t rmx = 64 * h32;
   const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
   // The score accumulators of a tile start from its per-key bias (centroid and extra tiles:
@@ -360,7 +389,9 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
   // 0 runs under the score products of half 1, the max of half 1 under the value products of
   // half 0.  Within a half, the exponentials of one 16-key step overlap the products of the
   // previous one.
-  auto compute = [&](int bf, f32x16_t* s) {
+  auto compute = [&](int bf, f32x16_t* s, auto rm) {
+    constexpr bool RM = decltype(rm)::value;   // V row-major (extra-token tiles)
+    const uint32_t ak_ = ak, av_ = RM ? rmo : av;
     const char* kt_ = reinterpret_cast<const char*>(sm.k[bf]);
     const char* vt_ = reinterpret_cast<const char*>(sm.v[bf]);
     __builtin_amdgcn_s_setprio(1);
@@ -368,12 +399,12 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
     for (int kt = 0; kt < 2; ++kt) {
       if constexpr (!QK8) {
         // S^T (keys 32kt..32kt+31) += K Q^T; K fragments of step ks+1 read during step ks
-        bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt_ + ak + kt * 32 * D * 2);
+        bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt_ + ak_ + kt * 32 * D * 2);
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
           bf16x8_t n = a;
           if (ks + 1 < D / 16)
-            n = *reinterpret_cast<const bf16x8_t*>(kt_ + ((ak ^ (32u * (ks + 1))) + kt * 32 * D * 2));
+            n = *reinterpret_cast<const bf16x8_t*>(kt_ + ((ak_ ^ (32u * (ks + 1))) + kt * 32 * D * 2));
           s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
           a = n;
         }
@@ -411,10 +442,21 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
       return pf;
     };
     auto vread = [&](int ks, bf16x8_t* va) {
-      const uint32_t off = av ^ (32u * ks);
+      const uint32_t off = av_ ^ (32u * ks);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
         va[dt] = *reinterpret_cast<const bf16x8_t*>(vt_ + off + dt * 32 * 128);
+    };
+    // one fragment of a row-major V tile: element e = V[16ks + 8(e/4) + 4h32 + e%4][32dt + c32]
+    auto vread_rm = [&](int ks, int dt) {
+      const char* base = vt_ + (av_ + ((64u * dt) ^ rmx)) + ks * 32 * D;
+      uint32_t x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        x[e] = *reinterpret_cast<const uint16_t*>(base + (8 * (e >> 2) + (e & 3)) * 2 * D);
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      const u32x4_t pk = {x[0] | (x[1] << 16), x[2] | (x[3] << 16), x[4] | (x[5] << 16), x[6] | (x[7] << 16)};
+      return __builtin_bit_cast(bf16x8_t, pk);
     };
     float mx = half_max(s[0]);
 #pragma unroll
@@ -422,18 +464,35 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
       rescale(mx);
       const float nm = m_run == -__builtin_inff() ? 0.f : -m_run;
       float psum = 0.f;
-      bf16x8_t va[D / 32], vb[D / 32];
-      vread(2 * kt, va);
-      const bf16x8_t p0 = probs(2 * kt, nm, psum);
-      vread(2 * kt + 1, vb);
-      const bf16x8_t p1 = probs(2 * kt + 1, nm, psum);
+      if constexpr (RM) {
+        const bf16x8_t p0 = probs(2 * kt, nm, psum);
+        const bf16x8_t p1 = probs(2 * kt + 1, nm, psum);
+        // one fragment in registers at a time (scheduling fences keep the reads from piling up)
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], p0, o[dt], 0, 0, 0);
-      if (kt == 0) mx = half_max(s[1]);
+        for (int dt = 0; dt < D / 32; ++dt) {
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread_rm(2 * kt, dt), p0, o[dt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kt == 0) mx = half_max(s[1]);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[dt], p1, o[dt], 0, 0, 0);
+        for (int dt = 0; dt < D / 32; ++dt) {
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread_rm(2 * kt + 1, dt), p1, o[dt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        bf16x8_t va[D / 32], vb[D / 32];
+        vread(2 * kt, va);
+        const bf16x8_t p0 = probs(2 * kt, nm, psum);
+        vread(2 * kt + 1, vb);
+        const bf16x8_t p1 = probs(2 * kt + 1, nm, psum);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], p0, o[dt], 0, 0, 0);
+        if (kt == 0) mx = half_max(s[1]);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[dt], p1, o[dt], 0, 0, 0);
+      }
       l_run += psum;
     }
   };
@@ -454,25 +513,49 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
     if (mine) load_bias(cur.kind != 0 ? sm.bias[bf][g] : sm.zero, s);
     const TileDesc nxt = it.next();
     if (nxt.kind != 3) issue(nxt, bf ^ 1);
-    if (mine) compute(bf, s);
+    if (mine) compute(bf, s, BoolC<false>{});
     if (nxt.kind == 3) break;
     cur = nxt;
     bf ^= 1;
   }
 
-  // ---- extra tokens: up to 4 gathered 64-token tiles per query block, loaded synchronously.
-  // K rows go straight to LDS; V rows pass through registers and are stored transposed (with
-  // the same key permutation and swizzle as the pre-transposed tiles).
+  // ---- bf16: the extra tokens, up to 4 tiles of 64 per query block (block 0's, then block
+  // 1's), gathered straight to LDS and double-buffered like the main loop's tiles
+  if constexpr (!QK8) {
+    // tile j: block 0's tiles 0 .. nx0-1, then block 1's
+    const int nx0 = (ne[0] + 63) / 64, nx = nx0 + (ne[1] + 63) / 64;
+    auto issue_tile = [&](int j) { issue_extra(j < nx0 ? 0 : 1, 64 * (j < nx0 ? j : j - nx0), j & 1); };
+    if (nx > 0) {
+      __syncthreads();                    // every wave is done with the main loop's buffers
+      issue_tile(0);
 #pragma unroll 1
-  for (int gg = 0; gg < G; ++gg) {
-    const int cnt = ne[gg];
-    const int* el = sm.eidx[gg];
+      for (int i = 0; i < nx; ++i) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const int gg = i < nx0 ? 0 : 1;
+        if (i + 1 < nx) issue_tile(i + 1);
+        if (wave_on && g == gg) {
+          f32x16_t s[2];
+          load_bias(sm.bias[i & 1][gg], s);
+          compute(i & 1, s, BoolC<true>{});
+        }
+      }
+    }
+  }
+
+  // ---- fp8-QK: the extra tokens, up to 4 gathered 64-token tiles per query block, loaded
+  // synchronously after the loop: E4M3 key rows (and their scale codes) from the quantised
+  // tiles; V rows through registers, stored transposed (with the same key permutation and
+  // swizzle as the pre-transposed tiles).
+  if constexpr (QK8) {
 #pragma unroll 1
-    for (int e0 = 0; e0 < cnt; e0 += 64) {
-      __syncthreads();
-      uint16_t* vd = sm.v[0];
-      if constexpr (QK8) {
-        // E4M3 key rows (and their scale codes) from the quantised tiles
+    for (int gg = 0; gg < G; ++gg) {
+      const int cnt = ne[gg];
+      const int* el = sm.eidx[gg];
+#pragma unroll 1
+      for (int e0 = 0; e0 < cnt; e0 += 64) {
+        __syncthreads();
+        uint16_t* vd = sm.v[0];
 #pragma unroll
         for (int u = 0; u < PER_THREAD8; ++u) {
           const int sl = (u * 4 + w) * 64 + l;
@@ -484,35 +567,29 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
               *reinterpret_cast<const uint4*>(trow + (tok % 64) * D + c * 16);
           if (c == 0) sm.ke[0][r] = trow[64 * D + tok % 64];
         }
-      }
 #pragma unroll
-      for (int u = 0; u < PER_THREAD; ++u) {
-        const int sl = (u * 4 + w) * 64 + l;
-        const int r = sl / KCH, c = sl % KCH;
-        const int e = e0 + r < cnt ? e0 + r : e0;               // padding rows reuse a real token
-        const uint32_t tok = static_cast<uint32_t>(el[e]);
-        if constexpr (!QK8) {
-          uint16_t* kd = reinterpret_cast<uint16_t*>(sm.k[0]);
-          const uint4 kv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Kb) +
-                                                           (size_t)tok * ksn_b + c * 16);
-          *reinterpret_cast<uint4*>(kd + r * D + kswz<D>(r, c) * 8) = kv;
-        }
-        const uint4 vv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Vb) +
-                                                         (size_t)tok * vsn_b + c * 16);
-        const uint16_t* vx = reinterpret_cast<const uint16_t*>(&vv);
-        const int pos = vt_pos(r);
+        for (int u = 0; u < PER_THREAD; ++u) {
+          const int sl = (u * 4 + w) * 64 + l;
+          const int r = sl / KCH, c = sl % KCH;
+          const int e = e0 + r < cnt ? e0 + r : e0;
+          const uint32_t tok = static_cast<uint32_t>(el[e]);
+          const uint4 vv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Vb) +
+                                                           (size_t)tok * vsn_b + c * 16);
+          const uint16_t* vx = reinterpret_cast<const uint16_t*>(&vv);
+          const int pos = vt_pos(r);
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int dr = c * 8 + x;                           // d row of the transposed tile
-          vd[dr * 64 + (vswz(dr, pos >> 3) << 3) + (pos & 7)] = vx[x];
+          for (int x = 0; x < 8; ++x) {
+            const int dr = c * 8 + x;                         // d row of the transposed tile
+            vd[dr * 64 + (vswz(dr, pos >> 3) << 3) + (pos & 7)] = vx[x];
+          }
         }
-      }
-      if (tid < 64) sm.bias[0][gg][tid] = e0 + tid < cnt ? 0.f : -__builtin_inff();
-      __syncthreads();
-      if (wave_on && g == gg) {
-        f32x16_t s[2];
-        load_bias(sm.bias[0][gg], s);
-        compute(0, s);
+        if (tid < 64) sm.bias[0][gg][tid] = e0 + tid < cnt ? 0.f : -__builtin_inff();
+        __syncthreads();
+        if (wave_on && g == gg) {
+          f32x16_t s[2];
+          load_bias(sm.bias[0][gg], s);
+          compute(0, s, BoolC<false>{});
+        }
       }
     }
   }
