@@ -170,11 +170,21 @@ def test_dense_limits(dtype, case):
 
 
 def test_few_candidates_for_extra_tokens():
-    # tau = -2 keeps almost every block: fewer candidate tokens than extra_tokens
+    # tau = -2 keeps almost every block: fewer candidate tokens than extra_tokens.  Some query
+    # blocks then have no extra token while their neighbour has some, the case where the
+    # attention kernel's extra-token loop starts with the second block of a pair.
     w = workload(1, dtype="bf16", d=128, H=2, tau=-2.0, extra_tokens=256)
     x = make_inputs(w)
     _, sel, _ = run_and_check(w, x, range(2))
-    assert (sel["extra_cnt"] < 256).any()
+    cnt = sel["extra_cnt"].reshape(2, -1)
+    assert (cnt < 256).any()
+    Mq = w.N // 64
+    starts_with_second = 0
+    for bh in range(2):
+        stride = int(np.argmin(sel["pair_plan"][bh])) + 1
+        for a, b in sa.pair_schedule(Mq, (0, 0), stride):
+            starts_with_second += int(b >= 0 and cnt[bh, a] == 0 and cnt[bh, b] > 0)
+    assert starts_with_second > 0
 
 
 @pytest.mark.parametrize("flags", [0, sa.FLAG_EXACT_EXTRA])
