@@ -71,6 +71,15 @@ def test_sol_bf16_extra_partial_tiles(extra):
     run_and_check(w, x, range(1))
 
 
+def test_sol_bf16_d64_extra_tokens():
+    # head dim 64: the attention kernel's 64-wide instance, with a partial extra-token tile
+    # (V of the gathered tokens read row-major at d = 64) and a dense run
+    w = workload(2, d=64, H=2, extra_tokens=96, dense_rows=(16384 - 512, 16384))
+    x = make_inputs(w, heads=[0, 1])
+    _, sel, _ = run_and_check(w, x, range(2))
+    assert (sel["extra_cnt"] == 96).any()
+
+
 def _sample(rng_seed, n_sparse=6, n_dense=2, n_flagged=2):
     # random sparse and dense query blocks, plus query blocks whose extra tokens were selected
     # by the exact pass after the sampled pass fell short (if any)
