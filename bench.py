@@ -246,7 +246,7 @@ def main():
 
     # one more (untimed) call with the library's per-call counters
     stats_t = torch.zeros(sa.NSTATS, dtype=torch.int64, device=dev)
-    call(stats=stats_t, flags=sa.FLAG_CHECK_FINITE)
+    call(stats=stats_t, flags=sa.FLAG_CHECK_FINITE | sa.FLAG_KEEP_SELECTION)
     torch.cuda.synchronize()
     call_stats = dict(zip(sa.STAT_NAMES, (int(x_) for x_ in stats_t.cpu().tolist())))
 

@@ -32,6 +32,7 @@ class SolattnError(RuntimeError):
 
 FLAG_EXACT_EXTRA = 1   # SOLATTN_FLAG_EXACT_EXTRA
 FLAG_CHECK_FINITE = 2  # SOLATTN_FLAG_CHECK_FINITE
+FLAG_KEEP_SELECTION = 4  # SOLATTN_FLAG_KEEP_SELECTION
 NSTATS = 8             # SOLATTN_NSTATS
 STAT_NAMES = ("kept_blocks", "selected_qblocks", "exact_pairs", "centroid_terms", "extra_tokens",
               "near_threshold", "exact_extra_qblocks", "nonfinite")
@@ -59,11 +60,16 @@ class Opts(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "total", "qbar", "kbar", "vbar", "scores", "kept_cnt", "kept_idx", "kept_bm", "mult", "cbias", "extra_cnt",
-        "extra_idx", "extra_buf", "extra_part", "extra_flag", "kbar_bf", "vbar_t", "v_t")] + [
-        ("Mq", ctypes.c_int), ("M", ctypes.c_int), ("Mpad", ctypes.c_int),
-        ("k8", ctypes.c_size_t), ("kb8", ctypes.c_size_t), ("pair_plan", ctypes.c_size_t),
-        ("extra_seed", ctypes.c_size_t)]
+        "total", "kept_cnt", "kept_bm", "kept_idx", "mult", "extra_cnt", "extra_idx", "extra_flag",
+        "scores", "qbar", "kbar", "vbar", "extra_buf", "extra_part", "extra_seed", "kbar_bf", "vbar_t",
+        "v_t", "k8", "kb8", "pair_plan")] + [
+        ("Mq", ctypes.c_int), ("M", ctypes.c_int), ("Mpad", ctypes.c_int)]
+
+
+class Selection(ctypes.Structure):
+    _fields_ = [("Mq", ctypes.c_int), ("M", ctypes.c_int), ("Mpad", ctypes.c_int)] + [
+        (n, ctypes.c_void_p) for n in ("kept_cnt", "kept_bm", "kept_idx", "mult", "extra_cnt",
+                                       "extra_idx", "extra_flag", "scores")]
 
 
 _lib = None
@@ -88,16 +94,20 @@ def lib() -> ctypes.CDLL:
     L.solattn_check_args.restype = i
     L.local3d_check_args.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(Opts)]
     L.local3d_check_args.restype = i
-    L.solattn_workspace_layout.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(WsLayout)]
+    L.solattn_workspace_layout.argtypes = [i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(WsLayout)]
     L.solattn_workspace_layout.restype = i
+    L.solattn_workspace_bytes_ex.argtypes = [i, i, i, i, i, i, i, i, i, i]
+    L.solattn_workspace_bytes_ex.restype = ctypes.c_size_t
     L.solattn_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
     L.solattn_workspace_bytes.restype = ctypes.c_size_t
-    L.solattn_workspace_layout_rows.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(WsLayout)]
-    L.solattn_workspace_layout_rows.restype = i
-    L.solattn_workspace_bytes_rows.argtypes = [i, i, i, i, i, i, i, i, i]
-    L.solattn_workspace_bytes_rows.restype = ctypes.c_size_t
+    L.solattn_selection_view.argtypes = [ctypes.POINTER(Opts), i, i, i, i, i, i, ctypes.POINTER(Selection)]
+    L.solattn_selection_view.restype = i
+    L.solattn_free_default_workspaces.argtypes = []
+    L.solattn_free_default_workspaces.restype = i
     L.solattn_status_string.argtypes = [i]
     L.solattn_status_string.restype = ctypes.c_char_p
+    L.solattn_last_error_detail.argtypes = []
+    L.solattn_last_error_detail.restype = ctypes.c_char_p
     L.solattn_last_error.argtypes = []
     L.solattn_last_error.restype = ctypes.c_char_p
     L.solattn_timing_enable.argtypes = [i]
@@ -118,7 +128,8 @@ def status_string(status: int) -> str:
 
 
 def last_error() -> str:
-    return lib().solattn_last_error().decode()
+    """Detail of the last failing call on this thread (solattn_last_error_detail)."""
+    return lib().solattn_last_error_detail().decode()
 
 
 def kernel_names():
@@ -138,20 +149,34 @@ def pair_schedule(Mq: int, dense=(0, 0), stride: int = 1):
 
 
 def workspace_layout(mode: int, dtype: int, B: int, H: int, N: int, d: int, block_q: int,
-                     block_k: int, q_rows: int | None = None) -> WsLayout:
+                     block_k: int, q_rows: int | None = None, extra_tokens: int = MAX_EXTRA) -> WsLayout:
     """Offsets of the intermediate buffers; q_rows: rows of a query-row window (default N)."""
     L = WsLayout()
     rows = N if q_rows is None else int(q_rows)
-    rc = lib().solattn_workspace_layout_rows(mode, dtype, B, H, N, d, block_q, block_k, rows,
-                                             ctypes.byref(L))
+    rc = lib().solattn_workspace_layout(mode, dtype, B, H, N, d, block_q, block_k, int(extra_tokens),
+                                        rows, ctypes.byref(L))
     if rc != OK:
         raise SolattnError(rc, "invalid workspace shape")
     return L
 
 
-def workspace_bytes(mode, dtype, B, H, N, d, block_q, block_k, q_rows=None) -> int:
+def workspace_bytes(mode, dtype, B, H, N, d, block_q, block_k, q_rows=None,
+                    extra_tokens=MAX_EXTRA) -> int:
+    """Bytes of a caller workspace for this call shape (solattn_workspace_bytes_ex)."""
     rows = N if q_rows is None else int(q_rows)
-    return int(lib().solattn_workspace_bytes_rows(mode, dtype, B, H, N, d, block_q, block_k, rows))
+    return int(lib().solattn_workspace_bytes_ex(mode, dtype, B, H, N, d, block_q, block_k,
+                                                int(extra_tokens), rows))
+
+
+def workspace_bytes_any(mode, B, H, N, d, block_q, block_k, extra_tokens) -> int:
+    """Bytes enough for a whole-sequence call of this shape in any dtype (solattn_workspace_bytes)."""
+    return int(lib().solattn_workspace_bytes(mode, B, H, N, d, block_q, block_k, int(extra_tokens)))
+
+
+def free_default_workspaces() -> None:
+    rc = lib().solattn_free_default_workspaces()
+    if rc != OK:
+        raise SolattnError(rc, last_error())
 
 
 def make_opts(dtype=BF16, strides=None, dense_rows=(0, 0), workspace=0, workspace_bytes=0,
@@ -220,12 +245,14 @@ def _check_tensor(name, t, shape, dtype):
         raise ValueError(f"{name}: the d axis must be contiguous")
 
 
-def alloc_workspace(mode, q, block_q, block_k, q_rows=None, qk_fp8=False):
-    """A workspace for a call on q's shape (or on the query-row window q_rows = (begin, end))."""
+def alloc_workspace(mode, q, block_q, block_k, q_rows=None, qk_fp8=False, extra_tokens=MAX_EXTRA):
+    """A workspace for a call on q's shape (or on the query-row window q_rows = (begin, end))
+    with up to extra_tokens extra tokens."""
     torch = _torch()
     B, H, N, d = q.shape
     rows = None if q_rows is None else q_rows[1] - q_rows[0]
-    nbytes = workspace_bytes(mode, _dtype_code(q, qk_fp8), B, H, N, d, block_q, block_k, rows)
+    nbytes = workspace_bytes(mode, _dtype_code(q, qk_fp8), B, H, N, d, block_q, block_k, rows,
+                             extra_tokens)
     return torch.empty(nbytes, dtype=torch.uint8, device=q.device)
 
 
@@ -241,7 +268,7 @@ def _call(mode, q, k, v, *, tau, keep_percent, block_q, block_k, sink_range, ext
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     _check_tensor("out", out, q.shape, q.dtype)
     if workspace is None:
-        workspace = alloc_workspace(mode, q, block_q, block_k, q_rows, qk_fp8)
+        workspace = alloc_workspace(mode, q, block_q, block_k, q_rows, qk_fp8, extra_tokens)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     strides = [tuple(t.stride()[:3]) for t in (q, k, v, out)]
@@ -311,15 +338,28 @@ def local3d_attn(q, k, v, *, grid, block_q=64, block_k=64, sink_range=0, extra_t
 
 def selection_views(workspace, mode, dtype, B, H, N, d, block_q, block_k, q_rows=None):
     """Views of a call's intermediate results inside its workspace tensor (torch, on device);
-    q_rows = (begin, end) for a call on a query-row window (its query blocks count from 0)."""
+    q_rows = (begin, end) for a call on a query-row window (its query blocks count from 0).
+    The selection comes from solattn_selection_view; kept_idx and mult hold the call's values
+    only when it ran with FLAG_KEEP_SELECTION (or on fp32 tensors).  scores: [BH, Mq, M] (the
+    padding columns of the library's rows are cut off)."""
     torch = _torch()
     L = workspace_layout(mode, dtype, B, H, N, d, block_q, block_k,
                          None if q_rows is None else q_rows[1] - q_rows[0])
     BH, Mq, M, Mpad = B * H, L.Mq, L.M, L.Mpad
+    base = workspace.data_ptr()
+    o = make_opts(dtype, workspace=base, workspace_bytes=workspace.numel(), q_rows=q_rows)
+    sv = Selection()
+    rc = lib().solattn_selection_view(ctypes.byref(o), mode, B, H, N, block_q, block_k, ctypes.byref(sv))
+    if rc != OK:
+        raise SolattnError(rc, last_error())
+    assert (sv.Mq, sv.M, sv.Mpad) == (Mq, M, Mpad)
 
     def view(off, count, dt, shape):
         nbytes = count * torch.tensor([], dtype=dt).element_size()
         return workspace[off:off + nbytes].view(dt).reshape(shape)
+
+    def sel(ptr, count, dt, shape):
+        return view(int(ptr) - base, count, dt, shape)
 
     extra = {}
     if L.pair_plan:
@@ -329,16 +369,24 @@ def selection_views(workspace, mode, dtype, B, H, N, d, block_q, block_k, q_rows
         qbar=view(L.qbar, BH * Mq * d, torch.float32, (BH, Mq, d)),
         kbar=view(L.kbar, BH * M * d, torch.float32, (BH, M, d)),
         vbar=view(L.vbar, BH * M * d, torch.float32, (BH, M, d)),
-        scores=view(L.scores, BH * Mq * M, torch.float32, (BH, Mq, M)),
-        kept_cnt=view(L.kept_cnt, BH * Mq, torch.int32, (BH, Mq)),
-        kept_idx=view(L.kept_idx, BH * Mq * M, torch.int32, (BH, Mq, M)),
-        kept_bm=view(L.kept_bm, BH * Mq * (Mpad // 64), torch.int64, (BH, Mq, Mpad // 64)),
-        mult=view(L.mult, BH * Mq * Mpad, torch.uint8, (BH, Mq, Mpad)),
-        cbias=view(L.cbias, BH * Mq * Mpad, torch.float32, (BH, Mq, Mpad)),
-        extra_cnt=view(L.extra_cnt, BH * Mq, torch.int32, (BH, Mq)),
-        extra_idx=view(L.extra_idx, BH * Mq * MAX_EXTRA, torch.int32, (BH, Mq, MAX_EXTRA)),
-        extra_flag=view(L.extra_flag, BH * Mq, torch.int32, (BH, Mq)),
+        scores=sel(sv.scores, BH * Mq * Mpad, torch.float32, (BH, Mq, Mpad))[:, :, :M],
+        kept_cnt=sel(sv.kept_cnt, BH * Mq, torch.int32, (BH, Mq)),
+        kept_idx=sel(sv.kept_idx, BH * Mq * M, torch.int32, (BH, Mq, M)),
+        kept_bm=sel(sv.kept_bm, BH * Mq * (Mpad // 64), torch.int64, (BH, Mq, Mpad // 64)),
+        mult=sel(sv.mult, BH * Mq * Mpad, torch.uint8, (BH, Mq, Mpad)),
+        extra_cnt=sel(sv.extra_cnt, BH * Mq, torch.int32, (BH, Mq)),
+        extra_idx=sel(sv.extra_idx, BH * Mq * MAX_EXTRA, torch.int32, (BH, Mq, MAX_EXTRA)),
+        extra_flag=sel(sv.extra_flag, BH * Mq, torch.int32, (BH, Mq)),
     )
+
+
+def kept_masks(sel_np, bh: int, M: int):
+    """[Mq, M] bool kept masks of (b, h) index bh from a numpy copy of selection_views' kept_bm
+    (the bitmap every call writes)."""
+    import numpy as np
+    words = sel_np["kept_bm"][bh].astype(np.int64).view(np.uint64)
+    bits = ((words[:, :, None] >> np.arange(64, dtype=np.uint64)[None, None, :]) & np.uint64(1))
+    return bits.reshape(words.shape[0], -1)[:, :M].astype(bool)
 
 
 def header_functions():

@@ -66,12 +66,14 @@ def _is_oom(exc) -> bool:
 
 
 def chunked_attention(method: str, q, k, v, *, chunk_rows: int, block_q: int = 64,
-                      block_k: int = 64, out=None, alloc=None, **params):
+                      block_k: int = 64, out=None, alloc=None, on_chunk=None, **params):
     """Run ``method`` ("sol", "sla" or "local3d") over [B, H, N, d] GPU tensors in chunks of
     ``chunk_rows`` query rows.  ``params`` go to the library call (tau, keep_percent, grid,
     sink_range, extra_tokens, dense_rows, flags, stream, qk_fp8).  ``alloc(nbytes)`` returns a uint8
     workspace tensor (default: torch.empty on q's device); an out-of-memory error from it or
-    from the call halves the chunk.  Returns (out, ChunkReport)."""
+    from the call halves the chunk.  ``on_chunk(begin, end, workspace)``, if given, is called
+    after each chunk's call was enqueued (e.g. to read the chunk's selection from its
+    workspace).  Returns (out, ChunkReport)."""
     import torch
 
     from . import _lib as L
@@ -89,7 +91,8 @@ def chunked_attention(method: str, q, k, v, *, chunk_rows: int, block_q: int = 6
     def attempt(begin, end):
         try:
             nbytes = L.workspace_bytes(modes[method], L._dtype_code(q, params.get("qk_fp8", False)),
-                                       B, H, N, d, block_q, block_k, end - begin)
+                                       B, H, N, d, block_q, block_k, end - begin,
+                                       params.get("extra_tokens", 0))
             ws = alloc(nbytes)
             calls[method](q, k, v, block_q=block_q, block_k=block_k, out=out, workspace=ws,
                           q_rows=(begin, end), **params)
@@ -97,6 +100,8 @@ def chunked_attention(method: str, q, k, v, *, chunk_rows: int, block_q: int = 6
             if _is_oom(exc):
                 raise ChunkTooLarge(str(exc)) from exc
             raise
+        if on_chunk is not None:
+            on_chunk(begin, end, ws)
 
     rep = run_chunks(N, block_q, chunk_rows, attempt)
     return out, rep

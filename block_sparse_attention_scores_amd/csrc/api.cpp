@@ -86,7 +86,7 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   if (!(r0 == 0 && r1 == 0) && !(r0 >= 0 && r0 < r1 && r1 <= N))
     return fail(SOLATTN_EINVAL, "query-row window [%d, %d) not inside [0, N]", r0, r1);
   const unsigned flags = opts ? opts->flags : 0u;
-  if (flags & ~(SOLATTN_FLAG_EXACT_EXTRA | SOLATTN_FLAG_CHECK_FINITE))
+  if (flags & ~(SOLATTN_FLAG_EXACT_EXTRA | SOLATTN_FLAG_CHECK_FINITE | SOLATTN_FLAG_KEEP_SELECTION))
     return fail(SOLATTN_EINVAL, "unknown flags 0x%x", flags);
   if ((flags & SOLATTN_FLAG_CHECK_FINITE) && !(opts && opts->stats))
     return fail(SOLATTN_EINVAL, "SOLATTN_FLAG_CHECK_FINITE needs opts->stats");
@@ -135,11 +135,13 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
   return SOLATTN_OK;
 }
 
-// q_rows: query rows of the computed window (N for the whole sequence).
-int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k, solattn_ws_layout* L,
-           int q_rows) {
+// q_rows: query rows of the computed window (N for the whole sequence).  The selection regions
+// come first; their offsets depend on (B, H, Mq, M) only.
+int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k, int extra_tokens,
+           int q_rows, solattn_ws_layout* L) {
   (void)mode;
   if (B < 1 || H < 1 || N < 1 || d < 1 || block_q < 1 || block_k < 1 || q_rows < 1 || q_rows > N ||
+      extra_tokens < 0 || extra_tokens > SOLATTN_MAX_EXTRA ||
       (dtype != SOLATTN_BF16 && dtype != SOLATTN_FP32 && dtype != SOLATTN_BF16_FP8QK))
     return SOLATTN_EINVAL;
   std::memset(L, 0, sizeof *L);
@@ -152,22 +154,25 @@ int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int blo
     off = align256(off + bytes);
     return at;
   };
+  L->kept_cnt = take(BH * Mq * 4);
+  L->kept_bm = take(BH * Mq * (Mpad / 64) * 8);
+  L->kept_idx = take(BH * Mq * M * 4);
+  L->mult = take(BH * Mq * Mpad);
+  L->extra_cnt = take(BH * Mq * 4);
+  L->extra_idx = take(BH * Mq * SOLATTN_MAX_EXTRA * 4);
+  L->extra_flag = take(BH * Mq * 4);
+  L->scores = take(BH * Mq * Mpad * 4);
   L->qbar = take(BH * Mq * d * 4);
   L->kbar = take(BH * M * d * 4);
   L->vbar = take(BH * M * d * 4);
-  L->scores = take(BH * Mq * M * 4);
-  L->kept_cnt = take(BH * Mq * 4);
-  L->kept_idx = take(BH * Mq * M * 4);
-  L->kept_bm = take(BH * Mq * (Mpad / 64) * 8);
-  L->mult = take(BH * Mq * Mpad);
-  L->cbias = take(BH * Mq * Mpad * 4);
-  L->extra_cnt = take(BH * Mq * 4);
-  L->extra_idx = take(BH * Mq * SOLATTN_MAX_EXTRA * 4);
+  if (dtype != SOLATTN_FP32 && block_q == 64) L->pair_plan = take(BH * solattn::PAIR_STRIDES * 8);
   int S, nl;
   solattn::extra_split(dtype == SOLATTN_FP32, B, H, Mq, &S, &nl);
-  L->extra_buf = take(BH * Mq * nl * solattn::EXTRA_CAP * 8);
-  L->extra_part = take(BH * Mq * nl * 4);
-  L->extra_flag = take(BH * Mq * 4);
+  // without extra tokens the candidate buffer only holds the per-call counters' partial sums
+  const size_t cand = extra_tokens > 0 ? BH * Mq * nl * solattn::EXTRA_CAP * 8 : solattn::stats_scratch_bytes();
+  L->extra_buf = take(std::max(cand, solattn::stats_scratch_bytes()));
+  L->extra_part = take(extra_tokens > 0 ? BH * Mq * nl * 4 : 4);
+  L->extra_seed = take(BH * Mq * 4);
   if (dtype != SOLATTN_FP32) {
     L->kbar_bf = take(BH * Mpad * d * 2);
     L->vbar_t = take(BH * Mpad * d * 2);
@@ -178,8 +183,6 @@ int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int blo
     L->k8 = take(BH * (size_t)M * tb);
     L->kb8 = take(BH * (size_t)(Mpad / 64) * tb);
   }
-  if (dtype != SOLATTN_FP32 && block_q == 64) L->pair_plan = take(BH * solattn::PAIR_STRIDES * 8);
-  L->extra_seed = take(BH * Mq * 4);
   L->total = off;
   L->Mq = Mq;
   L->M = M;
@@ -187,10 +190,17 @@ int layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int blo
   return SOLATTN_OK;
 }
 
-// Library-owned workspace per device (grow-only), used when the caller passes none.
+// Library-owned workspaces (grow-only), one per (device, stream), used when the caller passes
+// none.  The lock is held from the buffer lookup until the call's last launch is enqueued, so a
+// buffer is never freed while another thread is about to launch on it.
+struct DefaultWs {
+  int dev;
+  hipStream_t stream;
+  void* p;
+  size_t size;
+};
 std::mutex g_ws_mu;
-void* g_ws[64] = {};
-size_t g_ws_size[64] = {};
+std::vector<DefaultWs> g_ws;
 
 // Per-kernel timing.
 constexpr int NK = SOLATTN_NKERNELS;
@@ -230,10 +240,11 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   int r0 = opts ? opts->q_row_begin : 0, r1 = opts ? opts->q_row_end : 0;
   if (r0 == 0 && r1 == 0) r1 = N;
   solattn_ws_layout L;
-  layout(mode, dtype, B, H, N, d, block_q, block_k, &L, r1 - r0);
+  layout(mode, dtype, B, H, N, d, block_q, block_k, extra_tokens, r1 - r0, &L);
   hipStream_t stream = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
 
   char* ws = nullptr;
+  std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
   if (opts && opts->workspace) {
     if (opts->workspace_bytes < L.total)
       return fail(SOLATTN_EWORKSPACE, "workspace %zu bytes < %zu required", opts->workspace_bytes, L.total);
@@ -242,24 +253,31 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
     ws = static_cast<char*>(opts->workspace);
   } else {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(SOLATTN_EHIP, "hipGetDevice");
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    if (g_ws_size[dev] < L.total) {
-      if (g_ws[dev]) {
-        // earlier calls on any stream may still read the old buffer
-        hipError_t e = hipDeviceSynchronize();
-        if (e != hipSuccess) return fail(SOLATTN_EHIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
-        e = hipFree(g_ws[dev]);
-        g_ws[dev] = nullptr;
-        g_ws_size[dev] = 0;
-        if (e != hipSuccess) return fail(SOLATTN_EHIP, "hipFree: %s", hipGetErrorString(e));
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SOLATTN_EHIP, "hipGetDevice");
+    ws_lock.lock();
+    DefaultWs* e = nullptr;
+    for (DefaultWs& x : g_ws)
+      if (x.dev == dev && x.stream == stream) e = &x;
+    if (!e) {
+      g_ws.push_back(DefaultWs{dev, stream, nullptr, 0});
+      e = &g_ws.back();
+    }
+    if (e->size < L.total) {
+      if (e->p) {
+        // only calls on this stream use this buffer: let them finish before it is freed
+        hipError_t er = hipStreamSynchronize(stream);
+        if (er != hipSuccess) return fail(SOLATTN_EHIP, "hipStreamSynchronize: %s", hipGetErrorString(er));
+        er = hipFree(e->p);
+        e->p = nullptr;
+        e->size = 0;
+        if (er != hipSuccess) return fail(SOLATTN_EHIP, "hipFree: %s", hipGetErrorString(er));
       }
       void* p = nullptr;
       if (hipMalloc(&p, L.total) != hipSuccess) return fail(SOLATTN_EHIP, "hipMalloc(%zu) failed", L.total);
-      g_ws[dev] = p;
-      g_ws_size[dev] = L.total;
+      e->p = p;
+      e->size = L.total;
     }
-    ws = static_cast<char*>(g_ws[dev]);
+    ws = static_cast<char*>(e->p);
   }
 
   Problem P;
@@ -299,7 +317,7 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
   P.kept_idx = reinterpret_cast<int*>(ws + L.kept_idx);
   P.kept_bm = reinterpret_cast<uint64_t*>(ws + L.kept_bm);
   P.mult = reinterpret_cast<uint8_t*>(ws + L.mult);
-  P.cbias = reinterpret_cast<float*>(ws + L.cbias);
+  P.keep_lists = (dtype == SOLATTN_FP32 || (opts && (opts->flags & SOLATTN_FLAG_KEEP_SELECTION))) ? 1 : 0;
   P.extra_cnt = reinterpret_cast<int*>(ws + L.extra_cnt);
   P.extra_idx = reinterpret_cast<int*>(ws + L.extra_idx);
   P.extra_buf = reinterpret_cast<uint2*>(ws + L.extra_buf);
@@ -441,28 +459,75 @@ int local3d_check_args(const void* q, const void* k, const void* v, void* out, i
 }
 
 int solattn_workspace_layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k,
-                             solattn_ws_layout* out) {
+                             int extra_tokens, int q_rows, solattn_ws_layout* out) {
   if (!out) return SOLATTN_EINVAL;
-  return layout(mode, dtype, B, H, N, d, block_q, block_k, out, N);
+  return layout(mode, dtype, B, H, N, d, block_q, block_k, extra_tokens, q_rows, out);
 }
 
-size_t solattn_workspace_bytes(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k) {
+size_t solattn_workspace_bytes_ex(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k,
+                                  int extra_tokens, int q_rows) {
   solattn_ws_layout L;
-  if (layout(mode, dtype, B, H, N, d, block_q, block_k, &L, N) != SOLATTN_OK) return 0;
+  if (layout(mode, dtype, B, H, N, d, block_q, block_k, extra_tokens, q_rows, &L) != SOLATTN_OK) return 0;
   return L.total;
 }
 
-int solattn_workspace_layout_rows(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k,
-                                  int q_rows, solattn_ws_layout* out) {
-  if (!out) return SOLATTN_EINVAL;
-  return layout(mode, dtype, B, H, N, d, block_q, block_k, out, q_rows);
+size_t solattn_workspace_bytes(int mode, int B, int H, int N, int d, int block_q, int block_k, int extra_tokens) {
+  size_t most = 0;
+  for (int dt : {SOLATTN_BF16, SOLATTN_FP32, SOLATTN_BF16_FP8QK}) {
+    solattn_ws_layout L;
+    if (layout(mode, dt, B, H, N, d, block_q, block_k, extra_tokens, N, &L) != SOLATTN_OK) return 0;
+    most = std::max(most, L.total);
+  }
+  return most;
 }
 
-size_t solattn_workspace_bytes_rows(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k,
-                                    int q_rows) {
+int solattn_selection_view(const solattn_opts* opts, int mode, int B, int H, int N, int block_q, int block_k,
+                           solattn_selection* view) {
+  g_err.clear();
+  if (!opts || !view) return fail(SOLATTN_EINVAL, "selection_view: null opts or view");
+  if (opts->struct_size != (int)sizeof(solattn_opts))
+    return fail(SOLATTN_EINVAL, "opts->struct_size %d != %d", opts->struct_size, (int)sizeof(solattn_opts));
+  if (!opts->workspace) return fail(SOLATTN_EINVAL, "selection_view: opts->workspace is NULL");
+  if (mode != SOLATTN_MODE_SOL && mode != SOLATTN_MODE_SLA && mode != SOLATTN_MODE_LOCAL3D)
+    return fail(SOLATTN_EINVAL, "mode %d", mode);
+  int r0 = opts->q_row_begin, r1 = opts->q_row_end;
+  if (r0 == 0 && r1 == 0) r1 = N;
+  if (N < 1 || r0 < 0 || r1 <= r0 || r1 > N) return fail(SOLATTN_EINVAL, "selection_view: window [%d, %d)", r0, r1);
+  // the selection regions do not depend on the dtype, d or extra_tokens
   solattn_ws_layout L;
-  if (layout(mode, dtype, B, H, N, d, block_q, block_k, &L, q_rows) != SOLATTN_OK) return 0;
-  return L.total;
+  if (layout(mode, SOLATTN_BF16, B, H, N, 64, block_q, block_k, 0, r1 - r0, &L) != SOLATTN_OK)
+    return fail(SOLATTN_EINVAL, "selection_view: invalid shape");
+  char* ws = static_cast<char*>(opts->workspace);
+  view->Mq = L.Mq;
+  view->M = L.M;
+  view->Mpad = L.Mpad;
+  view->kept_cnt = reinterpret_cast<int32_t*>(ws + L.kept_cnt);
+  view->kept_bm = reinterpret_cast<uint64_t*>(ws + L.kept_bm);
+  view->kept_idx = reinterpret_cast<int32_t*>(ws + L.kept_idx);
+  view->mult = reinterpret_cast<uint8_t*>(ws + L.mult);
+  view->extra_cnt = reinterpret_cast<int32_t*>(ws + L.extra_cnt);
+  view->extra_idx = reinterpret_cast<int32_t*>(ws + L.extra_idx);
+  view->extra_flag = reinterpret_cast<int32_t*>(ws + L.extra_flag);
+  view->scores = reinterpret_cast<float*>(ws + L.scores);
+  return SOLATTN_OK;
+}
+
+int solattn_free_default_workspaces(void) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  int rc = SOLATTN_OK;
+  for (DefaultWs& e : g_ws) {
+    if (!e.p) continue;
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess || hipSetDevice(e.dev) != hipSuccess) {
+      rc = SOLATTN_EHIP;
+      continue;
+    }
+    if (hipDeviceSynchronize() != hipSuccess || hipFree(e.p) != hipSuccess) rc = SOLATTN_EHIP;
+    hipSetDevice(cur);
+  }
+  g_ws.clear();
+  if (rc != SOLATTN_OK) fail(rc, "free_default_workspaces: a HIP call failed");
+  return rc;
 }
 
 const char* solattn_status_string(int status) {
@@ -475,6 +540,8 @@ const char* solattn_status_string(int status) {
     default: return "unknown status";
   }
 }
+
+const char* solattn_last_error_detail(void) { return g_err.c_str(); }
 
 const char* solattn_last_error(void) { return g_err.c_str(); }
 

@@ -35,12 +35,12 @@ struct Problem {
   float* qbar;
   float* kbar;
   float* vbar;
-  float* scores;
+  float* scores;         // [B*H, Mq, Mpad]: row stride Mpad
   int* kept_cnt;
-  int* kept_idx;
+  int* kept_idx;         // ascending kept lists (written when keep_lists is set)
   uint64_t* kept_bm;     // kept blocks as a bitmap: word j/64, bit j%64
-  uint8_t* mult;
-  float* cbias;          // ln(centroid multiplicity) / scale (a raw-score offset), -inf where it is 0
+  uint8_t* mult;         // centroid multiplicities (written when keep_lists is set)
+  int keep_lists;        // write kept_idx and mult (fp32 tensors, or the caller asked to keep them)
   int* extra_cnt;
   int* extra_idx;
   uint2* extra_buf;      // per query block and candidate list: (score bits, token) candidates

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P, int rep
     __syncthreads();
     if (!any_row) return;
   }
-  const uint8_t* mrow = P.mult + grow * P.Mpad;
+  const uint64_t* bmrow = P.kept_bm + grow * (P.Mpad / 64);
   const float* kbase = static_cast<const float*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)h * P.k.sh;
   const int ts = (((N + S - 1) / S) + 127) / 128 * 128;       // tokens per slice
   const int t_lo = slice * ts, t_hi = min(N, t_lo + ts);
@@ -251,8 +251,11 @@ __global__ __launch_bounds__(256, 2) void extra_select_kernel(Problem P, int rep
 
   // scores of 32 consecutive tokens from tw for this lane's query block: register r holds token
   // tw + (r/4)*8 + (l/32)*4 + r%4 (the layout of the 16-bit pass's accumulator)
-  uint8_t mflag = 0;
-  auto load_keys = [&](int tw) { mflag = row_ok ? mrow[tw >> 6] : 0; };
+  uint8_t mflag = 0;      // 1: the block of token tw is not kept (its tokens are candidates)
+  auto load_keys = [&](int tw) {
+    const int j = tw >> 6;
+    mflag = row_ok ? static_cast<uint8_t>(((bmrow[j >> 6] >> (j & 63)) & 1ull) ^ 1ull) : 0;
+  };
   auto scores = [&](int tw, float* acc, auto&& prefetch) {
 #pragma unroll 1
     for (int r = 0; r < 16; ++r) {
@@ -1013,12 +1016,10 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) 
   for (int p = l; p < c; p += 64) {
     const int t = toks[p], bt = t >> 6;
     out[p] = t;
-    if (p == 0 || (toks[p - 1] >> 6) != bt) {
+    if (P.keep_lists && (p == 0 || (toks[p - 1] >> 6) != bt)) {
       int e = p + 1;
       while (e < c && (toks[e] >> 6) == bt) ++e;
-      const int m = 64 - (e - p);
-      mr[bt] = static_cast<uint8_t>(m);
-      P.cbias[row * P.Mpad + bt] = m > 0 ? __logf(static_cast<float>(m)) / P.scale : -__builtin_inff();
+      mr[bt] = static_cast<uint8_t>(64 - (e - p));
     }
   }
   if (l == 0) P.extra_cnt[row] = c;

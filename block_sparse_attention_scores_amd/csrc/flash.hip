@@ -69,6 +69,12 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t x, int lane) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// Orders one wave's LDS accesses before and after it.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Walks the main loop's work of a pair of query blocks: every key block kept by either of them,
 // in ascending order, then the centroid tiles.  The two kept-block bitmaps are held one 64-bit
 // word per lane (lane l: blocks 64l..64l+63), so finding the next tile is a ballot and a few
@@ -177,8 +183,6 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
     kw[gg] = (valid[gg] && l < nwords) ? P.kept_bm[row * nwords + l] : 0ull;
     elist[gg] = P.extra_idx + row * MAX_EXTRA;
   }
-  const float* cbrow[2] = {P.cbias + ((size_t)bh * P.Mq + qa) * P.Mpad,
-                           P.cbias + ((size_t)bh * P.Mq + (valid[1] ? qb[1] : qa)) * P.Mpad};
   int cent_sel = 0;
   if (P.mode == 0) {
 #pragma unroll
@@ -293,13 +297,33 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
       }
     }
     if (t.kind == 2 && w == 0) {
-      // the 64 biases of each query block: lanes 0-15 those of block 0 into sm.bias[bf][0],
-      // lanes 16-31 those of block 1 into sm.bias[bf][1] (lane i's 16 bytes land at 16 i)
+      // the 64 biases of each query block: ln(m) / scale for key block j = t.idx + l, where
+      // m = 64 minus the block's extra tokens for a block not kept, -inf where m = 0 (kept
+      // blocks, blocks taken whole as extra tokens, padding).  The extra tokens of the tile's
+      // 64 blocks are counted into the bias row itself (integer counters, LDS atomics from
+      // this wave only), then replaced by the biases.  The extra lists arrived in LDS with
+      // the first tile; the buffer is free (every wave has passed this iteration's barrier).
+      const int c = t.idx >> 6;
 #pragma unroll
       for (int gg = 0; gg < G; ++gg) {
         if (!valid[gg]) continue;
-        const __amdgpu_buffer_rsrc_t br = make_rsrc(cbrow[gg] + t.idx, 256);
-        if ((l >> 4) == gg) buf_to_lds16(br, (l & 15) * 16, reinterpret_cast<char*>(sm.bias[bf]));
+        int* cnt = reinterpret_cast<int*>(sm.bias[bf][gg]);
+        cnt[l] = 0;
+        wave_lds_sync();
+        const int n = gg ? ne[1] : ne[0];
+#pragma unroll
+        for (int e = 0; e < MAX_EXTRA / 64; ++e) {
+          const int p = l + 64 * e;
+          if (p < n) {
+            const int blk = sm.eidx[gg][p] >> 6;
+            if ((blk >> 6) == c) atomicAdd(&cnt[blk & 63], 1);
+          }
+        }
+        wave_lds_sync();
+        const uint64_t kword = readlane64(gg ? it.w1 : it.w0, c);
+        const int m = (t.idx + l < P.M && !((kword >> l) & 1ull)) ? 64 - cnt[l] : 0;
+        wave_lds_sync();
+        sm.bias[bf][gg][l] = m > 0 ? __logf(static_cast<float>(m)) / P.scale : -__builtin_inff();
       }
     }
   };

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(Problem P) {
     }
   }
   // accumulator register r of tile (a, b): row wi + 32a + (r/4)*8 + 4h + r%4, column wj + 32b + c32
-  float* S = P.scores + (size_t)bh * P.Mq * P.M;
+  float* S = P.scores + (size_t)bh * P.Mq * P.Mpad;     // rows of Mpad floats
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(Problem P) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = i0 + wi + 32 * a + (r / 4) * 8 + 4 * h + (r % 4);
-        if (i < P.Mq) S[(size_t)i * P.M + j] = acc[a][b][r] * P.scale;
+        if (i < P.Mq) S[(size_t)i * P.Mpad + j] = acc[a][b][r] * P.scale;
       }
     }
 }

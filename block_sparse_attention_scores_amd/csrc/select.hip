@@ -11,10 +11,14 @@
 //     is the centre, +-1 frame and +-1 block up/down/left/right stencil.
 //   Sink blocks and the diagonal block(s) are kept on top in every mode (node docs, sla
 //   table, and sink_conditioning row).  Query blocks in the dense row range keep every block.
-// The kept set is written twice: as an ascending index list and as a bitmap (bit j of word
-// j/64), which the attention kernel walks without touching memory.
-// One wave per row (four rows per workgroup); all reductions have a fixed order, so results
-// are deterministic.  Also writes each block's centroid multiplicity (0 = attended exactly).
+// The kept set is written as a bitmap (bit j of word j/64), which the attention kernel walks
+// without touching memory, with its count; the ascending index lists and the centroid
+// multiplicities are written only when asked for (fp32 tensors, or a caller keeping the
+// selection).
+// One wave per row (four rows per workgroup); the row's scores are read from memory once, into
+// registers (RU per lane, M <= 64 RU), and every pass (mean, deviation, threshold or radix
+// select, compaction) works on them; rows longer than that are read once per pass.  All
+// reductions have a fixed order, so results are deterministic.
 #include "common.h"
 #include "launch.h"
 
@@ -42,6 +46,9 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // fixed-order wave reduction (deterministic).
 constexpr int SEL_ROWS = 4;
 
+// RU > 0: the row (M <= 64 * RU blocks) is held in registers, block 64u + lane in register u.
+// RU == 0: the row is read from memory on every pass (any M).
+template <int RU>
 __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
   extern __shared__ uint32_t nbm_all[];   // local 3-D mode: one neighbourhood bitmap (Mpad/32 words) per wave
   __shared__ int hist_all[SEL_ROWS][256];
@@ -50,33 +57,47 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = blockIdx.x * SEL_ROWS + wv, bh = blockIdx.y;
   if (i >= P.Mq) return;                   // the whole wave: nothing below waits for other waves
-  const int M = P.M;
+  const int M = P.M, nu = (M + 63) >> 6, nw = P.Mpad >> 6;
   const size_t row = (size_t)bh * P.Mq + i;
-  const float* s = P.scores + row * M;
+  const float* s = P.scores + row * P.Mpad;
   int* kidx = P.kept_idx + row * M;
   uint8_t* mult = P.mult + row * P.Mpad;
-  float* cb = P.cbias + row * P.Mpad;
-  uint64_t* bm = P.kept_bm + row * (P.Mpad / 64);
-  // centroid logit offset in raw-score units: ln(block size) / scale
-  const float log2_bk = __logf(static_cast<float>(P.bk)) / P.scale;
+  uint64_t* bm = P.kept_bm + row * nw;
+  const bool lists = P.keep_lists != 0;
 
   const bool dense = i >= P.dense_q0 && i < P.dense_q1;
   if (dense || (P.mode == 0 && P.keep_all)) {
-    for (int j = lane; j < P.Mpad; j += 64) {
-      if (j < M) kidx[j] = j;
-      mult[j] = 0;
-      cb[j] = -__builtin_inff();
-    }
-    for (int wd = lane; wd < P.Mpad / 64; wd += 64) {
+    for (int wd = lane; wd < nw; wd += 64) {
       const int nb = M - 64 * wd;       // blocks of this word that exist
-      bm[wd] = nb >= 64 ? ~0ull : ((1ull << nb) - 1ull);
+      bm[wd] = nb >= 64 ? ~0ull : (nb > 0 ? ((1ull << nb) - 1ull) : 0ull);
     }
+    if (lists)
+      for (int j = lane; j < P.Mpad; j += 64) {
+        if (j < M) kidx[j] = j;
+        mult[j] = 0;
+      }
     if (lane == 0) {
       P.kept_cnt[row] = M;
       P.extra_cnt[row] = 0;
     }
     return;
   }
+
+  // the row's scores: block 64u + lane (padding columns up to Mpad exist but are never used)
+  float sv[RU > 0 ? RU : 1];
+  if constexpr (RU > 0) {
+    if (P.mode != 2) {
+#pragma unroll
+      for (int u = 0; u < RU; ++u) sv[u] = u < nu ? s[64 * u + lane] : 0.f;
+    }
+  }
+  auto score = [&](int u) -> float {
+    if constexpr (RU > 0) return sv[u];
+    else return s[64 * u + lane];
+  };
+  // loop bound over the row's 64-block groups: a constant (unrolled, registers indexed
+  // statically) when the row is held in registers
+  const int ulim = RU > 0 ? RU : nu;
 
   // forced blocks: the sinks and every key block overlapping this query block's tokens
   const int gi = i + P.q0;                       // global query block (rows are window-local)
@@ -92,13 +113,17 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
 
   if (P.mode == 0) {
     float acc = 0.f;
-    for (int j = lane; j < M; j += 64) acc += s[j];
+#pragma unroll
+    for (int u = 0; u < ulim; ++u)
+      if (u < nu && 64 * u + lane < M) acc += score(u);
     const float mu = wave_sum(acc) / static_cast<float>(M);
     float acc2 = 0.f;
-    for (int j = lane; j < M; j += 64) {
-      const float dv = s[j] - mu;
-      acc2 = fmaf(dv, dv, acc2);
-    }
+#pragma unroll
+    for (int u = 0; u < ulim; ++u)
+      if (u < nu && 64 * u + lane < M) {
+        const float dv = score(u) - mu;
+        acc2 = fmaf(dv, dv, acc2);
+      }
     const float var = wave_sum(acc2) / static_cast<float>(M);
     const float sd = sqrtf(var);
     theta = sd > 0.f ? fmaf(P.tau, sd, mu) : mu;
@@ -137,10 +162,13 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
         wave_lds_sync();
-        for (int j = lane; j < M; j += 64) {
-          if (forced(j)) continue;
-          const uint32_t key = float_key(s[j]);
-          if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+#pragma unroll
+        for (int u = 0; u < ulim; ++u) {
+          const int j = 64 * u + lane;
+          if (u < nu && j < M && !forced(j)) {
+            const uint32_t key = float_key(score(u));
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+          }
         }
         wave_lds_sync();
         // lane l holds digits 255-4l .. 252-4l; counts accumulate from the top digit down
@@ -179,41 +207,51 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
     }
   }
 
-  // ordered compaction of the kept blocks, 64 at a time: the keep ballot is the bitmap word
+  // ordered compaction of the kept blocks, 64 at a time: the keep ballot is the bitmap word u,
+  // which lane u keeps and writes at the end (one coalesced store per row)
   int base = 0, eq_base = 0;
-  for (int j0 = 0; j0 < M; j0 += 64) {
-    const int j = j0 + lane;
-    bool keep = false, eq = false;
-    if (j < M) {
-      if (forced(j)) {
-        keep = true;
-      } else if (P.mode == 0) {
-        keep = s[j] > theta;
-      } else if (P.mode == 2) {
-        keep = (nbm[j >> 5] >> (j & 31)) & 1u;
-      } else if (sla_any) {
-        const uint32_t key = float_key(s[j]);
-        keep = key > kstar;
-        eq = key == kstar;
+  uint64_t myword = 0;
+#pragma unroll
+  for (int u = 0; u < ulim; ++u) {
+    if (u < nu) {
+      const int j = 64 * u + lane;
+      bool keep = false, eq = false;
+      if (j < M) {
+        if (forced(j)) {
+          keep = true;
+        } else if (P.mode == 0) {
+          keep = score(u) > theta;
+        } else if (P.mode == 2) {
+          keep = (nbm[j >> 5] >> (j & 31)) & 1u;
+        } else if (sla_any) {
+          const uint32_t key = float_key(score(u));
+          keep = key > kstar;
+          eq = key == kstar;
+        }
       }
+      const uint64_t eqm = __ballot(eq);
+      if (eq && eq_base + lanes_below(eqm) < need_eq) keep = true;
+      eq_base += __popcll(eqm);
+      const uint64_t word = __ballot(keep);
+      if (RU > 0) {
+        myword = lane == u ? word : myword;
+      } else if (lane == 0) {
+        bm[u] = word;
+      }
+      if (lists) {
+        if (keep) kidx[base + lanes_below(word)] = j;
+        if (j < M) mult[j] = keep ? 0 : static_cast<uint8_t>(P.bk);
+      }
+      base += __popcll(word);
     }
-    const uint64_t eqm = __ballot(eq);
-    if (eq && eq_base + lanes_below(eqm) < need_eq) keep = true;
-    eq_base += __popcll(eqm);
-    const uint64_t word = __ballot(keep);
-    if (keep) kidx[base + lanes_below(word)] = j;
-    if (lane == 0) bm[j0 >> 6] = word;
-    if (j < M) {
-      mult[j] = keep ? 0 : static_cast<uint8_t>(P.bk);
-      cb[j] = keep ? -__builtin_inff() : log2_bk;
-    }
-    base += __popcll(word);
   }
-  for (int wd = ((M + 63) >> 6) + lane; wd < P.Mpad / 64; wd += 64) bm[wd] = 0ull;
-  for (int j = M + lane; j < P.Mpad; j += 64) {
-    mult[j] = 0;
-    cb[j] = -__builtin_inff();
+  if (RU > 0) {
+    if (lane < nw) bm[lane] = lane < nu ? myword : 0ull;
+  } else {
+    for (int wd = nu + lane; wd < nw; wd += 64) bm[wd] = 0ull;
   }
+  if (lists)
+    for (int j = M + lane; j < P.Mpad; j += 64) mult[j] = 0;
   if (lane == 0) {
     P.kept_cnt[row] = base;
     P.extra_cnt[row] = 0;
@@ -259,7 +297,13 @@ hipError_t launch_pair_plan(const Problem& P, hipStream_t stream) {
 hipError_t launch_block_select(const Problem& P, hipStream_t stream) {
   dim3 grid((P.Mq + SEL_ROWS - 1) / SEL_ROWS, P.B * P.H);
   const size_t lds = P.mode == 2 ? (size_t)SEL_ROWS * (P.Mpad / 32) * 4 : 0;
-  hipLaunchKernelGGL(block_select_kernel, grid, dim3(256), lds, stream, P);
+  // registers for the row: the smallest instance that holds it
+  if (P.mode == 2 || P.M > 64 * 64)
+    hipLaunchKernelGGL(block_select_kernel<0>, grid, dim3(256), lds, stream, P);
+  else if (P.M <= 64 * 16)
+    hipLaunchKernelGGL(block_select_kernel<16>, grid, dim3(256), lds, stream, P);
+  else
+    hipLaunchKernelGGL(block_select_kernel<64>, grid, dim3(256), lds, stream, P);
   return hipGetLastError();
 }
 

@@ -54,13 +54,19 @@ __global__ __launch_bounds__(256) void stats_rows_kernel(Problem P, long long* p
     acc[4] += ec;
     if (extra_ran) acc[6] += P.extra_flag[row] == 1 ? 1 : 0;
     if (P.mode == 0) {
-      const uint8_t* mult = P.mult + row * P.Mpad;
-      int c = 0;
-      for (int j = lane; j < M; j += 64) c += mult[j] > 0 ? 1 : 0;
-      acc[3] += nrows * wave_sum_i(c);
+      // centroid terms: every key block not kept, except blocks whose 64 tokens are all extra
+      // tokens (multiplicity 0).  The extra list is ascending and unique, so a block is whole
+      // exactly when its first token sits at position p and its last at p + 63.
+      const int* el = P.extra_idx + row * MAX_EXTRA;
+      int whole = 0;
+      for (int p = lane; p + 63 < ec; p += 64) {
+        const int t = el[p];
+        whole += ((t & 63) == 0 && el[p + 63] == t + 63) ? 1 : 0;
+      }
+      acc[3] += nrows * ((long long)(M - kc) - wave_sum_i(whole));
       if (!P.keep_all) {
         // the row's threshold, recomputed in fp32 (two passes, population deviation)
-        const float* s = P.scores + row * M;
+        const float* s = P.scores + row * P.Mpad;
         float a = 0.f;
         for (int j = lane; j < M; j += 64) a += s[j];
         const float mu = wave_sum_f(a) / static_cast<float>(M);
@@ -97,14 +103,18 @@ __global__ __launch_bounds__(256) void stats_finite_kernel(Problem P, long long*
   const T* base = static_cast<const T*>(t.p);
   constexpr int PER = 16 / sizeof(T);                 // elements per chunk
   const int cpr = P.d / PER;                          // chunks per row
-  const long chunks = (long)P.B * P.H * P.N * cpr;
+  // out: only the rows of the computed window (the others are not written by the call)
+  const bool is_out = blockIdx.y == 3;
+  const long tok0 = is_out ? (long)P.q0 * P.bq : 0;
+  const long ntok = is_out ? (long)P.Mq * P.bq : P.N;
+  const long chunks = (long)P.B * P.H * ntok * cpr;
   long long n = 0;
   for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < chunks; e += (long)gridDim.x * 256) {
     const long r = e / cpr;
     const int c = static_cast<int>(e - r * cpr);
-    const int b = static_cast<int>(r / ((long)P.H * P.N));
-    const int h = static_cast<int>((r / P.N) % P.H);
-    const long tok = r % P.N;
+    const int b = static_cast<int>(r / ((long)P.H * ntok));
+    const int h = static_cast<int>((r / ntok) % P.H);
+    const long tok = tok0 + r % ntok;
     const uint4 v = *reinterpret_cast<const uint4*>(base + (int64_t)b * t.sb + (int64_t)h * t.sh +
                                                     tok * t.sn + (int64_t)c * PER);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};

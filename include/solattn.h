@@ -42,7 +42,7 @@ extern "C" {
 #define SOLATTN_EINVAL     -1   /* an argument is out of its domain                        */
 #define SOLATTN_ENOTSUP    -2   /* valid, but this build does not implement the shape      */
 #define SOLATTN_EWORKSPACE -3   /* the caller's workspace is smaller than required        */
-#define SOLATTN_EHIP       -4   /* a HIP runtime or launch error (detail in last_error)    */
+#define SOLATTN_EHIP       -4   /* a HIP runtime or launch error (see last_error_detail)   */
 
 /* Element types of q, k, v and out (all four share one type). */
 #define SOLATTN_BF16 0
@@ -70,6 +70,17 @@ extern "C" {
  * [B, H, N, d] tensors, no dense rows, the null stream, a library-owned
  * workspace.  Set struct_size = sizeof(solattn_opts) and zero every field you
  * do not use.
+ *
+ * Workspace.  A caller-owned workspace (opts->workspace) must hold at least
+ * solattn_workspace_bytes_ex(...) bytes for the call's mode, dtype, shape,
+ * extra_tokens and row window (solattn_workspace_bytes(...) is enough for any
+ * dtype), be 256-byte aligned, and not be used by another call that may run at
+ * the same time.  The call allocates nothing then.  Without one, the library
+ * keeps one grow-only buffer per (device, stream): calls on one stream share it
+ * and are ordered by the stream; calls on different streams use different
+ * buffers.  Growing a stream's buffer first waits for that stream (so work
+ * still queued on the old buffer finishes before it is freed).  The buffers
+ * live until solattn_free_default_workspaces() or the end of the process.
  */
 typedef struct solattn_opts {
   int struct_size;
@@ -80,13 +91,13 @@ typedef struct solattn_opts {
   int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
   int dense_row_begin, dense_row_end;   /* query rows attending every key; empty if equal */
   void*  workspace;               /* device buffer owned by the caller, or NULL            */
-  size_t workspace_bytes;         /* its size; must be >= solattn_workspace_bytes(...)     */
+  size_t workspace_bytes;         /* its size; must be >= solattn_workspace_bytes_ex(...)  */
   void*  stream;                  /* hipStream_t; NULL = null stream                       */
   unsigned flags;                 /* SOLATTN_FLAG_* bits; 0 = defaults                       */
   int64_t* stats;                 /* device int64[SOLATTN_NSTATS] for per-call counters, or NULL */
   /* Query-row window: only rows [q_row_begin, q_row_end) are computed (both multiples of
    * block_q); the other rows of out are left untouched.  Keys are always all N rows.  Both 0
-   * means every row.  The workspace then covers the window only (see the _rows layout
+   * means every row.  The workspace then covers the window only (q_rows of the layout
    * calls), which is how a caller splits a long sequence into row chunks that fit in memory.
    * Dense rows are given in whole-sequence coordinates and intersected with the window; the
    * intermediate buffers (qbar, scores, lists, ...) hold the window's query blocks from 0. */
@@ -108,6 +119,15 @@ typedef struct solattn_opts {
  * returns SOLATTN_EINVAL.
  */
 #define SOLATTN_FLAG_CHECK_FINITE 2u
+
+/*
+ * SOLATTN_FLAG_KEEP_SELECTION: also write the kept key blocks as ascending index lists
+ * (kept_idx) and every key block's centroid multiplicity (mult), so that a caller can read the
+ * whole selection after the call through solattn_selection_view.  Without it a bf16 call writes
+ * only what its kernels use: the kept sets as bitmaps, their counts and the extra-token lists.
+ * fp32 calls always write both.  The output does not depend on the flag.
+ */
+#define SOLATTN_FLAG_KEEP_SELECTION 4u
 
 /*
  * Per-call counters (opts->stats != NULL): a device array of SOLATTN_NSTATS int64 values,
@@ -202,75 +222,111 @@ int local3d_check_args(const void* q, const void* k, const void* v, void* out,
                        const solattn_opts* opts);
 
 /*
- * Workspace.  Byte offsets (from the workspace start, each 256-byte aligned) of
- * the intermediate buffers of one call, which stay readable after the call
- * until the workspace is reused:
- *   qbar      fp32 [B*H, Mq, d]    pooled queries
- *   kbar      fp32 [B*H, M, d]     pooled keys
- *   vbar      fp32 [B*H, M, d]     pooled values
- *   scores    fp32 [B*H, Mq, M]    block scores s_ij (not written by local3d_attn_fwd)
- *   kept_cnt  int32 [B*H, Mq]      number of kept key blocks (M for dense query blocks)
- *   kept_idx  int32 [B*H, Mq, M]   kept key-block indices, ascending, first kept_cnt valid
- *   kept_bm   uint64 [B*H, Mq, Mpad/64] the same kept set as a bitmap (bit j%64 of word j/64)
- *   mult      uint8 [B*H, Mq, Mpad] centroid multiplicity of each key block (0 = attended exactly)
- *   cbias     fp32 [B*H, Mq, Mpad] ln(multiplicity) * sqrt(d): the centroid term's logit offset
- *             in raw q.k units, -inf where the multiplicity is 0
- *   extra_cnt int32 [B*H, Mq]      number of extra tokens
- *   extra_idx int32 [B*H, Mq, 256] extra token indices, ascending, first extra_cnt valid
- *   extra_buf, extra_part: scratch of the extra-token selection (candidate lists per query
- *             block: one per token slice for 16-bit tensors, one per slice and wave for fp32;
- *             and their lengths); extra_buf also holds the partial sums of the per-call
- *             counters when they are requested
- *   extra_seed uint32 [B*H, Mq]    scratch of the extra-token selection (16-bit tensors): the
- *             threshold each query block's first pass starts from, seeded from a sample of
- *             the keys, as an order-preserving key of the fp32 score
- *   extra_flag int32 [B*H, Mq]     1 where the extra-token selection's first pass, whose
+ * Workspace layout.  Byte offsets (from the workspace start, each 256-byte aligned) of the
+ * intermediate buffers of one call, which stay readable after the call until the workspace is
+ * reused.  Mq = query blocks of the computed rows (the window, or N/block_q), M = N/block_k,
+ * Mpad = M rounded up to a multiple of 64.  The selection comes first and its offsets depend
+ * only on (B, H, Mq, M): they are the same for every dtype, d and extra_tokens.
+ *   kept_cnt  int32 [B*H, Mq]         number of kept key blocks (M for dense query blocks)
+ *   kept_bm   uint64 [B*H, Mq, Mpad/64] the kept set as a bitmap (bit j%64 of word j/64)
+ *   kept_idx  int32 [B*H, Mq, M]      kept key-block indices, ascending, first kept_cnt valid
+ *                                     (written with SOLATTN_FLAG_KEEP_SELECTION, or fp32)
+ *   mult      uint8 [B*H, Mq, Mpad]   centroid multiplicity of each key block: tokens of the
+ *                                     block not attended exactly, 0 for kept blocks (same
+ *                                     condition as kept_idx)
+ *   extra_cnt int32 [B*H, Mq]         number of extra tokens
+ *   extra_idx int32 [B*H, Mq, 256]    extra token indices, ascending, first extra_cnt valid
+ *   extra_flag int32 [B*H, Mq]        1 where the extra-token selection's first pass, whose
  *             threshold is seeded from a sample of the keys, kept fewer candidates than the
  *             selection needs, so that the query block was selected again with every
  *             candidate competing (the result is exact either way)
- *   kbar_bf   bf16 [B*H, Mpad, d], vbar_t bf16 [B*H, Mpad/64, d, 64], v_t bf16
- *             [B*H, M, d, 64]: operand copies for the attention kernel (bf16 only)
- *   k8, kb8   E4M3 tiles [B*H, M] and [B*H, Mpad/64] of 64 * d bytes (64 rows) followed by
- *             the 64 rows' scale codes e + 127 (SOLATTN_BF16_FP8QK only)
+ *   scores    fp32 [B*H, Mq, Mpad]    block scores s_ij (row stride Mpad; columns >= M are
+ *                                     padding; not written by local3d_attn_fwd)
+ * Then the rest:
+ *   qbar      fp32 [B*H, Mq, d]    pooled queries
+ *   kbar      fp32 [B*H, M, d]     pooled keys
+ *   vbar      fp32 [B*H, M, d]     pooled values
  *   pair_plan int64 [B*H, 8]: for pairing strides s = 1..8, the kept-block union summed over
  *             the pairs of query blocks that one attention workgroup takes together (with
  *             stride s, block t of each run of 2s non-dense query blocks pairs with block t+s);
  *             each head's workgroups use the stride with the least sum.  Scheduling only: no
  *             output depends on it (bf16 tensors with block_q 64 only; offset 0 otherwise)
- * Mq = N/block_q, M = N/block_k, Mpad = M rounded up to a multiple of 64.
+ *   extra_buf, extra_part: scratch of the extra-token selection (candidate lists per query
+ *             block: one per token slice for 16-bit tensors, one per slice and wave for fp32;
+ *             and their lengths; only the per-call counters' scratch when extra_tokens is 0);
+ *             extra_buf also holds the partial sums of the per-call counters
+ *   extra_seed uint32 [B*H, Mq]    scratch of the extra-token selection (16-bit tensors): the
+ *             threshold each query block's first pass starts from, seeded from a sample of
+ *             the keys, as an order-preserving key of the fp32 score
+ *   kbar_bf   bf16 [B*H, Mpad, d], vbar_t bf16 [B*H, Mpad/64, d, 64], v_t bf16
+ *             [B*H, M, d, 64]: operand copies for the attention kernel (bf16 only)
+ *   k8, kb8   E4M3 tiles [B*H, M] and [B*H, Mpad/64] of 64 * d bytes (64 rows) followed by
+ *             the 64 rows' scale codes e + 127 (SOLATTN_BF16_FP8QK only)
  */
 typedef struct solattn_ws_layout {
   size_t total;
-  size_t qbar, kbar, vbar, scores, kept_cnt, kept_idx, kept_bm, mult, cbias, extra_cnt, extra_idx;
-  size_t extra_buf, extra_part;  /* scratch of the extra-token selection                   */
-  size_t extra_flag;             /* int32 [B*H, Mq]: 1 = selection redone exactly            */
-  size_t kbar_bf, vbar_t, v_t;
+  size_t kept_cnt, kept_bm, kept_idx, mult, extra_cnt, extra_idx, extra_flag, scores;
+  size_t qbar, kbar, vbar;
+  size_t extra_buf, extra_part, extra_seed;
+  size_t kbar_bf, vbar_t, v_t, k8, kb8, pair_plan;
   int Mq, M, Mpad;
-  size_t k8, kb8;                /* SOLATTN_BF16_FP8QK only: E4M3 key and pooled-key tiles  */
-  size_t pair_plan;              /* 16-bit types with block_q 64 only (else 0): int64
-                                    [B*H, 8], see above                                      */
-  size_t extra_seed;             /* uint32 [B*H, Mq]: seeded threshold keys, see above       */
 } solattn_ws_layout;
 
-/* Fills *layout for a call of this shape.  Returns SOLATTN_OK or SOLATTN_EINVAL. */
-int solattn_workspace_layout(int mode, int dtype, int B, int H, int N, int d,
-                             int block_q, int block_k, solattn_ws_layout* layout);
+/*
+ * Fills *layout for a call of this mode, dtype (SOLATTN_BF16, SOLATTN_FP32 or
+ * SOLATTN_BF16_FP8QK), shape and extra_tokens (0..256) over a window of q_rows query rows
+ * (q_rows = N: the whole sequence; 1 <= q_rows <= N).  Returns SOLATTN_OK or SOLATTN_EINVAL.
+ */
+int solattn_workspace_layout(int mode, int dtype, int B, int H, int N, int d, int block_q, int block_k,
+                             int extra_tokens, int q_rows, solattn_ws_layout* layout);
 
-/* Total workspace bytes for a call of this shape (0 if the shape is invalid). */
-size_t solattn_workspace_bytes(int mode, int dtype, int B, int H, int N, int d,
-                               int block_q, int block_k);
+/* Total bytes of that layout (0 if the arguments are invalid). */
+size_t solattn_workspace_bytes_ex(int mode, int dtype, int B, int H, int N, int d, int block_q,
+                                  int block_k, int extra_tokens, int q_rows);
 
-/* The same two calls for a query-row window of q_rows rows (opts->q_row_begin/end);
- * q_rows = N gives the whole-sequence layout.  q_rows in [1, N]. */
-int solattn_workspace_layout_rows(int mode, int dtype, int B, int H, int N, int d,
-                                  int block_q, int block_k, int q_rows, solattn_ws_layout* layout);
-size_t solattn_workspace_bytes_rows(int mode, int dtype, int B, int H, int N, int d,
-                                    int block_q, int block_k, int q_rows);
+/*
+ * Workspace bytes a whole-sequence call of this shape needs with any dtype (the largest of
+ * the three layouts); 0 if the arguments are invalid.
+ */
+size_t solattn_workspace_bytes(int mode, int B, int H, int N, int d, int block_q, int block_k,
+                               int extra_tokens);
+
+/*
+ * The selection of a call, as device pointers into its workspace (valid once the call has
+ * completed on its stream, until the workspace is reused).  Shapes and conditions as in the
+ * layout above; kept_idx and mult hold the call's values only if it ran with
+ * SOLATTN_FLAG_KEEP_SELECTION (or on fp32 tensors).
+ */
+typedef struct solattn_selection {
+  int Mq, M, Mpad;
+  int32_t*  kept_cnt;
+  uint64_t* kept_bm;
+  int32_t*  kept_idx;
+  uint8_t*  mult;
+  int32_t*  extra_cnt;
+  int32_t*  extra_idx;
+  int32_t*  extra_flag;
+  float*    scores;
+} solattn_selection;
+
+/*
+ * Fills *view from opts->workspace (required: a caller-owned workspace) and the query-row window
+ * in opts (q_row_begin/q_row_end; both 0 for the whole sequence), for a call of this mode and
+ * shape.  Host only: no device access.  Returns SOLATTN_OK or SOLATTN_EINVAL.
+ */
+int solattn_selection_view(const solattn_opts* opts, int mode, int B, int H, int N, int block_q,
+                           int block_k, solattn_selection* view);
+
+/* Frees the library-owned default workspaces (after waiting for the device).  Returns a status. */
+int solattn_free_default_workspaces(void);
 
 /* Static text for a status code. */
 const char* solattn_status_string(int status);
 
-/* Thread-local detail of the last failing call on this thread ("" if none). */
+/* Thread-local detail of the last failing call on this thread, naming the bad argument or the
+ * failing HIP call ("" if the last call succeeded). */
+const char* solattn_last_error_detail(void);
+/* The same text (the name earlier versions of this header used). */
 const char* solattn_last_error(void);
 
 /*

@@ -37,6 +37,8 @@ MODES = {"sol": sa.MODE_SOL, "sla": sa.MODE_SLA, "local3d": sa.MODE_LOCAL3D}
 
 def run_gpu(mode, q, k, v, *, block_q, block_k, tau=1.3, keep_percent=10.0, sink_range=0,
             extra_tokens=0, dense_rows=(0, 0), flags=0, grid=None):
+    # the kept lists and multiplicities are written on request only; the parity checks read them
+    flags |= sa.FLAG_KEEP_SELECTION
     if mode == "local3d":
         out, ws = sa.local3d_attn(q, k, v, grid=grid, block_q=block_q, block_k=block_k,
                                   sink_range=sink_range, extra_tokens=extra_tokens,
@@ -97,8 +99,9 @@ def check_head(mode, ref, sel, bh, *, x_in, d, block_k, tau, keep_percent, sink_
         bound = 1e-5 * scale * (np.abs(ref["qbar"]) @ np.abs(ref["kbar"]).T) + 1e-30
         ds = np.abs(sel["scores"][bh].astype(np.float64) - ref["scores"])
         assert (ds <= bound).all(), f"score error {ds.max()} > bound"
-    # masks
+    # masks: the ascending lists and the bitmap the attention kernel walks hold the same sets
     gmask = gpu_kept_mask(sel, bh, M)
+    assert np.array_equal(gmask, sa.kept_masks(sel, bh, M)), "kept lists and bitmap differ"
     s = ref["scores"]
     for i in range(Mq):
         if ref["dense"][i]:

@@ -25,9 +25,65 @@ def check(mode=0, q=QP, k=KP, v=VP, o=OP, B=1, H=2, N=4096, d=64, tau=1.3, keep=
 def test_exports_every_declared_symbol():
     L = sa.lib()
     names = sa.header_functions()
-    assert {"sol_attn_fwd", "sla_attn_fwd", "solattn_workspace_bytes"} <= set(names)
+    # the calls of the boundary's specification, by name
+    assert {"sol_attn_fwd", "sla_attn_fwd", "solattn_workspace_bytes", "solattn_status_string",
+            "solattn_last_error_detail", "solattn_selection_view"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_last_error_detail_names_the_argument():
+    assert check(extra=300) == sa.EINVAL
+    detail = sa.lib().solattn_last_error_detail().decode()
+    assert "extra_tokens" in detail and detail == sa.lib().solattn_last_error().decode()
+    assert check() == sa.OK
+    assert sa.lib().solattn_last_error_detail().decode() == ""
+
+
+def test_keep_selection_flag_is_accepted():
+    assert check(opts=sa.make_opts(flags=sa.FLAG_KEEP_SELECTION)) == sa.OK
+    assert check(opts=sa.make_opts(flags=sa.FLAG_KEEP_SELECTION | sa.FLAG_EXACT_EXTRA)) == sa.OK
+    assert check(opts=sa.make_opts(flags=8)) == sa.EINVAL
+
+
+def test_workspace_bytes_any_dtype_and_extra_tokens():
+    # the specification's call: (mode, B, H, N, d, block_q, block_k, extra_tokens), enough for
+    # any dtype; the candidate lists of the extra-token selection only when extra_tokens > 0
+    for ex in (0, 64, 256):
+        any_ = sa.workspace_bytes_any(0, 1, 4, 16384, 128, 64, 64, ex)
+        per = [sa.workspace_bytes(0, dt, 1, 4, 16384, 128, 64, 64, None, ex)
+               for dt in (sa.BF16, sa.FP32, sa.BF16_FP8QK)]
+        assert any_ == max(per) > 0
+    assert sa.workspace_bytes(0, sa.BF16, 1, 4, 16384, 128, 64, 64, None, 0) < \
+        sa.workspace_bytes(0, sa.BF16, 1, 4, 16384, 128, 64, 64, None, 64)
+    assert sa.workspace_bytes_any(0, 1, 4, 16384, 128, 64, 64, 257) == 0
+    assert sa.workspace_bytes_any(0, 1, 4, 16384, 128, 64, 64, -1) == 0
+
+
+def test_selection_view_points_into_the_workspace():
+    base = 1 << 40
+    o = sa.make_opts(workspace=base, workspace_bytes=1 << 30)
+    v = sa.Selection()
+    assert sa.lib().solattn_selection_view(ctypes.byref(o), 0, 1, 2, 4096, 64, 64, ctypes.byref(v)) == sa.OK
+    L = sa.workspace_layout(0, sa.BF16, 1, 2, 4096, 128, 64, 64)
+    assert (v.Mq, v.M, v.Mpad) == (64, 64, 64)
+    for name in ("kept_cnt", "kept_bm", "kept_idx", "mult", "extra_cnt", "extra_idx", "extra_flag",
+                 "scores"):
+        assert getattr(v, name) == base + getattr(L, name), name
+    # the same offsets for every dtype, d and extra_tokens
+    for dt, d, ex in ((sa.FP32, 64, 0), (sa.BF16_FP8QK, 128, 256), (sa.BF16, 64, 64)):
+        L2 = sa.workspace_layout(0, dt, 1, 2, 4096, d, 64, 64, extra_tokens=ex)
+        assert (L2.kept_cnt, L2.kept_bm, L2.extra_idx, L2.scores) == (L.kept_cnt, L.kept_bm, L.extra_idx, L.scores)
+    # a window: its query blocks only
+    o = sa.make_opts(workspace=base, workspace_bytes=1 << 30, q_rows=(1024, 2048))
+    assert sa.lib().solattn_selection_view(ctypes.byref(o), 0, 1, 2, 4096, 64, 64, ctypes.byref(v)) == sa.OK
+    assert v.Mq == 16
+    # no workspace, or a bad window: an error naming it
+    o = sa.make_opts()
+    assert sa.lib().solattn_selection_view(ctypes.byref(o), 0, 1, 2, 4096, 64, 64, ctypes.byref(v)) == sa.EINVAL
+    assert "workspace" in sa.last_error()
+    o = sa.make_opts(workspace=base, workspace_bytes=1 << 30, q_rows=(2048, 1024))
+    assert sa.lib().solattn_selection_view(ctypes.byref(o), 0, 1, 2, 4096, 64, 64, ctypes.byref(v)) == sa.EINVAL
 
 
 def test_valid_arguments_pass():
@@ -119,7 +175,7 @@ def test_stats_and_flag_validation():
     assert check(opts=sa.make_opts(flags=sa.FLAG_CHECK_FINITE)) == sa.EINVAL
     assert "stats" in sa.last_error()
     assert check(opts=sa.make_opts(stats=(1 << 33) + 4)) == sa.EINVAL
-    assert check(opts=sa.make_opts(flags=4)) == sa.EINVAL
+    assert check(opts=sa.make_opts(flags=8)) == sa.EINVAL
     assert "flags" in sa.last_error()
     assert check(opts=sa.make_opts(flags=sa.FLAG_EXACT_EXTRA | sa.FLAG_CHECK_FINITE, stats=1 << 33)) == sa.OK
 
@@ -154,14 +210,16 @@ def test_fp8qk_layout():
     tb = 64 * 128 + 64
     v_t_bytes = 2 * 64 * 128 * 64 * 2
     assert f8.k8 >= bf.v_t + v_t_bytes and f8.kb8 - f8.k8 >= 2 * 64 * tb
-    assert f8.pair_plan - f8.kb8 >= 2 * 1 * tb
+    assert f8.total - f8.kb8 >= 2 * 1 * tb
 
 
 def test_pair_plan_layout():
     # the pairing sums exist for the 16-bit kernel with 64-row query blocks only
+    # (ahead of the extra-token scratch, so that its offset does not depend on extra_tokens)
     bf = sa.workspace_layout(0, sa.BF16, 1, 2, 4096, 128, 64, 64)
-    assert bf.pair_plan > bf.v_t and bf.total - bf.pair_plan >= 2 * sa.PAIR_STRIDES * 8
+    assert bf.pair_plan > bf.vbar and bf.extra_buf - bf.pair_plan >= 2 * sa.PAIR_STRIDES * 8
     assert bf.pair_plan % 256 == 0
+    assert sa.workspace_layout(0, sa.BF16, 1, 2, 4096, 128, 64, 64, extra_tokens=0).pair_plan == bf.pair_plan
     assert sa.workspace_layout(0, sa.FP32, 1, 2, 4096, 128, 64, 64).pair_plan == 0
     assert sa.workspace_layout(1, sa.BF16, 1, 2, 4096, 128, 128, 64).pair_plan == 0
     assert sa.workspace_layout(0, sa.BF16_FP8QK, 1, 2, 4096, 128, 64, 64).pair_plan > 0
@@ -182,15 +240,19 @@ def test_page_parameter_ranges_are_accepted():
 def test_workspace_layout():
     L = sa.workspace_layout(sa.MODE_SOL, sa.BF16, 1, 24, 65536, 128, 64, 64)
     assert (L.Mq, L.M, L.Mpad) == (1024, 1024, 1024)
-    offs = [L.qbar, L.kbar, L.vbar, L.scores, L.kept_cnt, L.kept_idx, L.kept_bm, L.mult, L.cbias, L.extra_cnt,
-            L.extra_idx, L.extra_buf, L.extra_part, L.extra_flag, L.kbar_bf, L.vbar_t, L.v_t]
+    offs = [L.kept_cnt, L.kept_bm, L.kept_idx, L.mult, L.extra_cnt, L.extra_idx, L.extra_flag, L.scores,
+            L.qbar, L.kbar, L.vbar, L.extra_buf, L.extra_part, L.extra_seed, L.kbar_bf, L.vbar_t, L.v_t]
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs) and L.total > L.v_t
-    assert L.scores - L.vbar >= 24 * 1024 * 128 * 4
+    assert L.qbar - L.scores >= 24 * 1024 * 1024 * 4        # scores rows of Mpad floats
+    assert L.kbar - L.qbar >= 24 * 1024 * 128 * 4
     a = sa.workspace_bytes(0, 0, 1, 24, 16384, 128, 64, 64)
     b = sa.workspace_bytes(0, 0, 1, 24, 32768, 128, 64, 64)
     assert 0 < a < b
     assert sa.workspace_bytes(0, 0, 0, 24, 16384, 128, 64, 64) == 0
+    # rows of ragged length: M = 100 key blocks, scores padded to Mpad = 128 per row
+    Lr = sa.workspace_layout(sa.MODE_SOL, sa.BF16, 1, 1, 6400, 128, 64, 64)
+    assert (Lr.M, Lr.Mpad) == (100, 128) and Lr.qbar - Lr.scores >= 100 * 128 * 4
     Lf = sa.workspace_layout(sa.MODE_SLA, sa.FP32, 1, 2, 4096, 64, 128, 64)
     assert Lf.Mpad == 64 and Lf.v_t == 0
 
