@@ -21,6 +21,7 @@ NKERNELS = 5
 
 
 PAIR_STRIDES = 8           # candidate pairing strides of the bf16 attention kernel
+NOALLOC_SCRATCH_BYTES = 64 << 20   # SOLATTN_NOALLOC_SCRATCH_BYTES
 
 
 class SolattnError(RuntimeError):
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.sol_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, ctypes.POINTER(Opts)]
     L.sol_attn_fwd.restype = i
+    L.sol_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, ctypes.POINTER(Opts)]
+    L.sol_attn_fwd_noalloc.restype = i
     L.sla_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, ctypes.POINTER(Opts)]
     L.sla_attn_fwd.restype = i
     L.local3d_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(Opts)]
@@ -309,6 +312,34 @@ def sol_attn(q, k, v, *, tau=1.3, block_q=64, block_k=64, sink_range=0, extra_to
                   workspace=workspace, stream=stream, flags=flags, stats=stats, q_rows=q_rows,
                   qk_fp8=qk_fp8)
     return (o, ws) if return_workspace else o
+
+
+def sol_attn_noalloc(q, k, v, *, tau=1.3, block_q=64, block_k=64, sink_range=0, extra_tokens=0,
+                     dense_rows=(0, 0), out=None, stream=None, flags=0, stats=None, q_rows=None,
+                     qk_fp8=False):
+    """sol-attn forward through sol_attn_fwd_noalloc: the library's own scratch buffer is the
+    workspace, nothing is allocated by the call (out must then be given by callers that cannot
+    allocate; None allocates it here, in torch).  Raises SolattnError with EWORKSPACE when the
+    call does not fit in NOALLOC_SCRATCH_BYTES."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    for n, t in (("k", k), ("v", v)):
+        _check_tensor(n, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape, q.dtype)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _check_tensor("out", out, q.shape, q.dtype)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    strides = [tuple(t.stride()[:3]) for t in (q, k, v, out)]
+    opts = make_opts(_dtype_code(q, qk_fp8), strides, dense_rows, 0, 0, stream, flags,
+                     stats.data_ptr() if stats is not None else 0, q_rows)
+    rc = lib().sol_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
+                                    float(tau), block_q, block_k, sink_range, extra_tokens,
+                                    ctypes.byref(opts))
+    if rc != OK:
+        raise SolattnError(rc, last_error())
+    return out
 
 
 def sla_attn(q, k, v, *, keep_percent=10.0, block_q=128, block_k=64, sink_range=0, extra_tokens=0,

@@ -226,9 +226,11 @@ hipEvent_t take_event() {
   return e;
 }
 
+// no_events: record no timing events even while timing is enabled (the allocation-free entry
+// point, which must not create HIP events).
 int run(int mode, const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
         float tau, float keep_percent, int block_q, int block_k, int sink_range, int extra_tokens,
-        const solattn_opts* opts, const int* grid = nullptr) {
+        const solattn_opts* opts, const int* grid = nullptr, bool no_events = false) {
   g_err.clear();
   Strides st[4];
   const int no_grid[3] = {0, 0, 0};
@@ -340,7 +342,7 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
     return fail(SOLATTN_ENOTSUP, "stats: candidate buffer smaller than the counters' scratch");
 
   std::unique_lock<std::mutex> tl(g_t_mu);
-  const bool timing = g_timing;
+  const bool timing = g_timing && !no_events;
   TimedCall tc;
   std::memset(&tc, 0, sizeof tc);
   auto release = [&]() {
@@ -413,6 +415,38 @@ int run(int mode, const void* q, const void* k, const void* v, void* out, int B,
 }
 
 }  // namespace
+
+namespace solattn {
+
+int set_error(int code, const char* detail) { return fail(code, "%s", detail); }
+
+int run_sol_on_buffer(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                      float tau, int block_q, int block_k, int sink_range, int extra_tokens,
+                      const solattn_opts* opts, void* ws, size_t ws_bytes) {
+  solattn_opts o;
+  if (opts) {
+    o = *opts;
+  } else {
+    std::memset(&o, 0, sizeof o);
+    o.struct_size = sizeof o;
+  }
+  const int dtype = o.dtype;
+  int r0 = o.q_row_begin, r1 = o.q_row_end;
+  if (r0 == 0 && r1 == 0) r1 = N;
+  solattn_ws_layout L;
+  if (layout(SOLATTN_MODE_SOL, dtype, B, H, N, d, block_q, block_k, extra_tokens, r1 - r0, &L) != SOLATTN_OK)
+    return fail(SOLATTN_EINVAL, "invalid shape");
+  if (L.total > ws_bytes)
+    return fail(SOLATTN_EWORKSPACE,
+                "sol_attn_fwd_noalloc: this call needs %zu bytes of workspace; the library's scratch holds %zu "
+                "(use sol_attn_fwd with a workspace, or a query-row window)", L.total, ws_bytes);
+  o.workspace = ws;
+  o.workspace_bytes = ws_bytes;
+  return run(SOLATTN_MODE_SOL, q, k, v, out, B, H, N, d, tau, 100.f, block_q, block_k, sink_range, extra_tokens,
+             &o, nullptr, true);
+}
+
+}  // namespace solattn
 
 extern "C" {
 

@@ -204,6 +204,30 @@ int local3d_attn_fwd(const void* q, const void* k, const void* v, void* out,
                      const solattn_opts* opts);
 
 /*
+ * Allocation-free sol-attn forward, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.  The same call and
+ * result as sol_attn_fwd, but its workspace is a scratch buffer the library holds in device
+ * memory: SOLATTN_NOALLOC_SCRATCH_BYTES per GPU, one copy on every GPU the library runs this
+ * call on, held until the process ends.  The call allocates nothing (no hipMalloc or hipFree,
+ * no HIP events, no library allocation).
+ *   opts->workspace must be NULL (SOLATTN_EINVAL otherwise); every other option works as in
+ *   sol_attn_fwd, including the query-row window, which bounds the workspace a call needs.
+ *   A call whose workspace (solattn_workspace_bytes_ex for its dtype, shape, extra_tokens and
+ *   window) exceeds SOLATTN_NOALLOC_SCRATCH_BYTES returns SOLATTN_EWORKSPACE before anything
+ *   runs, with the sizes in the error detail.
+ *   Every call on one GPU uses that GPU's one buffer, and the buffer keeps the last call's
+ *   intermediates (nothing in it needs clearing between calls): calls that may overlap on one
+ *   GPU (different streams, or different host threads without ordering) race on it and must
+ *   be serialised by the caller.  Calls ordered on one stream are safe.
+ * Returns a status code.
+ */
+#define SOLATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int sol_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                         int B, int H, int N, int d, float tau,
+                         int block_q, int block_k, int sink_range, int extra_tokens,
+                         const solattn_opts* opts);
+
+/*
  * Host-only argument check: the exact validation sol_attn_fwd / sla_attn_fwd
  * perform, without launching anything.  mode is SOLATTN_MODE_SOL or
  * SOLATTN_MODE_SLA (keep_percent is ignored for sol, tau for sla);

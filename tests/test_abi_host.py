@@ -262,3 +262,20 @@ def test_status_strings_and_kernel_names():
     assert "workspace" in sa.status_string(sa.EWORKSPACE)
     assert sa.kernel_names() == ["block_pool", "block_score", "block_select", "extra_select",
                                  "sparse_flash_fwd"]
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    import re
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "solattn.h")).read()
+    m = re.search(r"#define SOLATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == sa.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_validates_before_any_device_call():
+    # invalid arguments and a caller workspace are refused on the host (no GPU here)
+    L = sa.lib()
+    assert L.sol_attn_fwd_noalloc(QP, KP, VP, OP, 1, 2, 4096, 64, float("nan"), 64, 64, 0, 0, None) == sa.EINVAL
+    assert "tau" in sa.last_error()
+    o = sa.make_opts(workspace=1 << 40, workspace_bytes=1 << 30)
+    assert L.sol_attn_fwd_noalloc(QP, KP, VP, OP, 1, 2, 4096, 64, 1.3, 64, 64, 0, 0, ctypes.byref(o)) == sa.EINVAL
+    assert "workspace" in sa.last_error()
