@@ -82,6 +82,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak probes")
+    ap.add_argument("--no-headline", dest="headline", action="store_false",
+                    help="skip the N=202752 headline workload (timed after the default one)")
+    ap.add_argument("--headline-steps", type=int, default=5)
     return ap.parse_args()
 
 
@@ -119,12 +123,14 @@ def cpu_baseline(w, x, heads=(0,), n_sparse=24, n_dense=4, seed=7):
         p["grid"] = (w.T, w.Hh, w.Ww)
     t_sel = []
     t_sparse, t_dense = [], []
+    refs = {}
     rng = np.random.default_rng(seed)
     for h in heads:
         xin = [a[0, h].astype(np.float64) for a in (x.q, x.k, x.v)]
         t0 = time.perf_counter()
         ref = solattn.head_forward(w.mode, *xin, **p, want_out=False)
         t_sel.append(time.perf_counter() - t0)
+        refs[h] = ref
         sel = (ref["kept"], ref["extra"])
         sp = np.flatnonzero(~ref["dense"])
         dn = np.flatnonzero(ref["dense"])
@@ -151,7 +157,185 @@ def cpu_baseline(w, x, heads=(0,), n_sparse=24, n_dense=4, seed=7):
               f"{len(t_sparse)} sparse + {len(t_dense)} dense query blocks attended "
               f"({per_sparse * 1e3:.1f} / {per_dense * 1e3:.1f} ms each); extrapolated to "
               f"{BH} heads x {Mq} query blocks")
-    return dict(value=total * 1e3, unit="ms", cores=int(cores), kind="oracle", sample=sample)
+    return dict(value=total * 1e3, unit="ms", cores=int(cores), kind="oracle", sample=sample), refs
+
+
+def selection_check(w, sel, refs):
+    """The GPU's selection against the oracle's on the heads the CPU leg computed: kept-mask
+    bits that differ, extra-token set differences (on query blocks whose masks agree), and the
+    oracle's blocks within 1e-4 sigma of their row's threshold (sol)."""
+    import block_sparse_attention_scores_amd as sa
+    from oracle import solattn
+    M = w.N // w.block_k
+    flips = eflips = near = rows = 0
+    for h, ref in refs.items():
+        g = sa.kept_masks(sel, h, M)
+        cnt, idx = sel["extra_cnt"][h], sel["extra_idx"][h]
+        for i in range(g.shape[0]):
+            if ref["dense"][i]:
+                continue
+            rows += 1
+            d = int((g[i] != ref["kept"][i]).sum())
+            flips += d
+            if d == 0 and w.extra_tokens > 0:
+                a_ = set(idx[i, :cnt[i]].tolist())
+                eflips += len(a_ ^ set(np.asarray(ref["extra"][i]).tolist()))
+            if w.mode == "sol":
+                mu, sd = solattn.row_stats(ref["scores"][i])
+                near += int((np.abs(ref["scores"][i] - (mu + w.tau * sd)) <= 1e-4 * sd).sum())
+    return dict(heads=sorted(int(h) for h in refs), rows=rows, mask_flips=flips,
+                extra_flips=eflips, near_threshold_oracle=near)
+
+
+def measured_peaks(torch, sa, dev):
+    """What the matrix cores and HBM deliver here: a bf16 and an fp32 matrix-instruction loop
+    and a 1 GiB device copy (solattn_peak_probe), best of five launches each."""
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    out = {}
+    for kind, iters, name, scale in ((0, 400, "bf16_mfma_TFLOPs", 1e12), (1, 40, "fp32_mfma_TFLOPs", 1e12),
+                                     (2, 1, "copy_GBs", 1e9)):
+        best = 0.0
+        for rep in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            work = sa.peak_probe(kind, buf, iters)
+            e1.record()
+            torch.cuda.synchronize()
+            if rep:                                 # the first launch warms up
+                best = max(best, work / (e0.elapsed_time(e1) * 1e-3) / scale)
+        out[name] = round(best, 1)
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
+def kernel_rooflines(w, kern, sel, call_stats, qk_fp8, peaks):
+    """Each kernel against its roofline: spec peak (frac) and the peak measured here
+    (frac_measured).  Algorithmic work per the hot-path table: pool reads Q, K, V once and
+    writes the three fp32 means; select reads the score matrix once and writes counts and the
+    kept sets (bitmaps); score and the extra-token passes count their products (the extra
+    pass twice: hi and lo parts of the pooled query); the attention counts exact pairs only."""
+    BH, Mq, M = w.B * w.H, w.N // w.block_q, w.N // w.block_k
+    Mpad = (M + 63) // 64 * 64
+    es = 2 if w.dtype == "bf16" else 4
+    mb = peaks or {}
+
+    def rate(name, work, unit_scale, bound, peak, mpeak, **extra):
+        if name not in kern:
+            return
+        t = kern[name]["avg_ms"] * 1e-3
+        ach = work / t / unit_scale
+        key = "achieved_GBs" if bound == "hbm" else "achieved_TFLOPs"
+        kern[name].update(bound=bound, **{key: round(ach, 2)}, frac=round(ach / peak, 4), **extra)
+        if mpeak:
+            kern[name]["frac_measured"] = round(ach / mpeak, 4)
+
+    pool_alg = BH * (3 * w.N * w.d * es + (Mq + 2 * M) * w.d * 4)
+    pool_impl = pool_alg + (BH * (w.N * w.d * 2 + 2 * Mpad * w.d * 2) if w.dtype == "bf16" else 0)
+    rate("block_pool", pool_alg, 1e9, "hbm", PEAK_HBM_GBS, mb.get("copy_GBs"),
+         algorithmic_bytes=pool_alg, impl_bytes=pool_impl,
+         impl_frac=round(pool_impl / (kern.get("block_pool", {}).get("avg_ms", 1) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+    rate("block_score", 2.0 * BH * Mq * M * w.d, 1e12, "fp32", PEAK_FP32_TFLOPS, mb.get("fp32_mfma_TFLOPs"))
+    sel_alg = BH * Mq * (M * 4 + 8 + Mpad // 8)
+    rate("block_select", sel_alg, 1e9, "hbm", PEAK_HBM_GBS, mb.get("copy_GBs"), algorithmic_bytes=sel_alg)
+    rate("extra_select", 2.0 * 2.0 * BH * Mq * w.N * w.d, 1e12, "mfma", PEAK_BF16_TFLOPS, mb.get("bf16_mfma_TFLOPs"))
+    f_exact = 4.0 * w.d * call_stats["exact_pairs"]
+    # the fp8-QK flavour runs half of the exact work (Q K^T) at the fp8 peak and half (P V) at
+    # the bf16 peak: its ceiling is the work-weighted harmonic mix of the two
+    peak = PEAK_BF16_TFLOPS if not qk_fp8 else 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+    rate("sparse_flash_fwd", f_exact, 1e12, "mfma", peak, None if qk_fp8 else mb.get("bf16_mfma_TFLOPs"))
+    t_flash = kern["sparse_flash_fwd"]["avg_ms"] * 1e-3
+    ach = f_exact / t_flash / 1e12
+    roof = dict(bound="mfma", achieved=round(ach, 2), peak=round(peak, 1), unit="TFLOP/s",
+                frac=round(ach / peak, 4), traffic=measured_traffic(w.name),
+                kernel="sparse_flash_fwd", algorithmic_flop=f_exact)
+    if peaks and not qk_fp8:
+        roof["measured_peak"] = peaks["bf16_mfma_TFLOPs"]
+        roof["frac_measured_peak"] = round(ach / peaks["bf16_mfma_TFLOPs"], 4)
+    return roof
+
+
+def run_workload(w, a, torch, sa, dev, steps, warmup, keep_inputs=False):
+    """Generate the inputs, run `warmup` untimed and `steps` timed calls (one event pair per call
+    and per-kernel events inside the library), then one untimed call with the per-call counters
+    and the kept lists.  Returns the measurements."""
+    from gen import make_inputs
+    log(f"[bench] generating {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}")
+    t0 = time.perf_counter()
+    x = make_inputs(w)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+    if w.dtype == "bf16":
+        to = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k, v = to(x.q_bits), to(x.k_bits), to(x.v_bits)
+    else:
+        q, k, v = (torch.from_numpy(t).to(dev) for t in (x.q, x.k, x.v))
+    if not keep_inputs:
+        x = None
+    mode = {"sol": sa.MODE_SOL, "sla": sa.MODE_SLA, "local3d": sa.MODE_LOCAL3D}[w.mode]
+    out = torch.empty_like(q)
+    ws = sa.alloc_workspace(mode, q, w.block_q, w.block_k, qk_fp8=a.qk_fp8, extra_tokens=w.extra_tokens)
+
+    def call(**extra):
+        common = dict(block_q=w.block_q, block_k=w.block_k, sink_range=w.sink_range,
+                      extra_tokens=w.extra_tokens, dense_rows=w.dense_rows, out=out,
+                      workspace=ws, qk_fp8=a.qk_fp8, **extra)
+        if w.mode == "sol":
+            sa.sol_attn(q, k, v, tau=w.tau, **common)
+        elif w.mode == "local3d":
+            sa.local3d_attn(q, k, v, grid=(w.T, w.Hh, w.Ww), **common)
+        else:
+            sa.sla_attn(q, k, v, keep_percent=w.keep_percent, **common)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({warmup} calls)")
+
+    sa.timing_read()                 # drop anything recorded before
+    sa.timing_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    marks[0].record()
+    for i in range(steps):
+        call()
+        marks[i + 1].record()
+    end.record()
+    torch.cuda.synchronize()
+    per_call = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
+    t_wall = time.perf_counter() - t_wall
+    sa.timing_enable(False)
+    per_kernel = sa.timing_read()
+    ms_per_call = start.elapsed_time(end) / steps
+    log(f"[bench] {steps} calls: {ms_per_call:.3f} ms/call (wall {t_wall / steps * 1e3:.3f})")
+
+    if a.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 1 GiB device copies")
+
+    # one more (untimed) call with the library's per-call counters and the kept lists
+    stats_t = torch.zeros(sa.NSTATS, dtype=torch.int64, device=dev)
+    call(stats=stats_t, flags=sa.FLAG_CHECK_FINITE | sa.FLAG_KEEP_SELECTION)
+    torch.cuda.synchronize()
+    call_stats = dict(zip(sa.STAT_NAMES, (int(x_) for x_ in stats_t.cpu().tolist())))
+    dcode = sa.FP32 if w.dtype != "bf16" else (sa.BF16_FP8QK if a.qk_fp8 else sa.BF16)
+    views = sa.selection_views(ws, mode, dcode, w.B, w.H, w.N, w.d, w.block_q, w.block_k)
+    keep = ("kept_cnt", "kept_bm", "extra_cnt", "extra_idx", "mult")
+    sel = {k_: views[k_].cpu().numpy() for k_ in keep}
+    kern = {}
+    for name, (ms, n) in per_kernel.items():
+        if n:
+            kern[name] = dict(avg_ms=ms / n, launches=n)
+    del q, k, v, out, ws, views
+    torch.cuda.empty_cache()
+    return dict(x=x, ms_per_call=ms_per_call, per_call=per_call, kern=kern, call_stats=call_stats, sel=sel)
 
 
 def main():
@@ -163,7 +347,7 @@ def main():
 
     import torch
     import block_sparse_attention_scores_amd as sa
-    from gen import make_inputs, workload
+    from gen import workload
 
     ov = {}
     if a.tau is not None:
@@ -183,131 +367,41 @@ def main():
             raise SystemExit("--qk-fp8 needs a bf16 workload")
         w = workload(a.config, name=w.name + "-fp8qk", **ov)
     dev = torch.device("cuda:0")
-    log(f"[bench] generating {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}")
-    t0 = time.perf_counter()
-    x = make_inputs(w)
-    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
-    if w.dtype == "bf16":
-        to = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
-        q, k, v = to(x.q_bits), to(x.k_bits), to(x.v_bits)
-    else:
-        q, k, v = (torch.from_numpy(t).to(dev) for t in (x.q, x.k, x.v))
-    mode = {"sol": sa.MODE_SOL, "sla": sa.MODE_SLA, "local3d": sa.MODE_LOCAL3D}[w.mode]
-    out = torch.empty_like(q)
-    ws = sa.alloc_workspace(mode, q, w.block_q, w.block_k, qk_fp8=a.qk_fp8)
 
-    def call(**extra):
-        common = dict(block_q=w.block_q, block_k=w.block_k, sink_range=w.sink_range,
-                      extra_tokens=w.extra_tokens, dense_rows=w.dense_rows, out=out,
-                      workspace=ws, qk_fp8=a.qk_fp8, **extra)
-        if w.mode == "sol":
-            sa.sol_attn(q, k, v, tau=w.tau, **common)
-        elif w.mode == "local3d":
-            sa.local3d_attn(q, k, v, grid=(w.T, w.Hh, w.Ww), **common)
-        else:
-            sa.sla_attn(q, k, v, keep_percent=w.keep_percent, **common)
-
-    def step():
-        call()
-
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({a.warmup} calls)")
-
-    sa.timing_read()                 # drop anything recorded before
-    sa.timing_enable(True)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record()
-    marks[0].record()
-    for i in range(a.steps):
-        step()
-        marks[i + 1].record()
-    end.record()
-    torch.cuda.synchronize()
-    per_call = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(a.steps)])
-    t_wall = time.perf_counter() - t_wall
-    sa.timing_enable(False)
-    per_kernel = sa.timing_read()
-    ms_per_call = start.elapsed_time(end) / a.steps
-    log(f"[bench] {a.steps} calls: {ms_per_call:.3f} ms/call (wall {t_wall / a.steps * 1e3:.3f})")
-
-    if a.copy_calibration:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("[bench] copy calibration: 3 x 1 GiB device copies")
-
-    # one more (untimed) call with the library's per-call counters
-    stats_t = torch.zeros(sa.NSTATS, dtype=torch.int64, device=dev)
-    call(stats=stats_t, flags=sa.FLAG_CHECK_FINITE | sa.FLAG_KEEP_SELECTION)
-    torch.cuda.synchronize()
-    call_stats = dict(zip(sa.STAT_NAMES, (int(x_) for x_ in stats_t.cpu().tolist())))
-
-    dcode = sa.FP32 if w.dtype != "bf16" else (sa.BF16_FP8QK if a.qk_fp8 else sa.BF16)
-    views = sa.selection_views(ws, mode, dcode, w.B, w.H, w.N,
-                               w.d, w.block_q, w.block_k)
-    sel = {k_: v_.cpu().numpy() for k_, v_ in views.items()}
+    r = run_workload(w, a, torch, sa, dev, a.steps, a.warmup, keep_inputs=not a.no_cpu_baseline)
+    peaks = None
+    if not a.no_peaks:
+        peaks = measured_peaks(torch, sa, dev)
+        log(f"[bench] measured peaks: {peaks}")
+    kern, call_stats, sel = r["kern"], r["call_stats"], r["sel"]
     exact_pairs, cent_terms, kept_frac = selection_stats(sel, w, w.B, w.H)
-    f_exact = 4.0 * w.d * exact_pairs
-    f_cent = 4.0 * w.d * cent_terms
-    BH, Mq, M = w.B * w.H, w.N // w.block_q, w.N // w.block_k
-    es = 2 if w.dtype == "bf16" else 4
+    f_exact = 4.0 * w.d * call_stats["exact_pairs"]
+    f_cent = 4.0 * w.d * call_stats["centroid_terms"]
+    roof = kernel_rooflines(w, kern, sel, call_stats, a.qk_fp8, peaks)
 
-    kern = {}
-    for name, (ms, n) in per_kernel.items():
-        if n:
-            kern[name] = dict(avg_ms=ms / n, launches=n)
-    t_flash = kern["sparse_flash_fwd"]["avg_ms"] * 1e-3
-    ach = f_exact / t_flash / 1e12
-    # the fp8-QK flavour runs half of the exact work (Q K^T) at the fp8 peak and half (P V) at
-    # the bf16 peak: its ceiling is the work-weighted harmonic mix of the two
-    peak = PEAK_BF16_TFLOPS if not a.qk_fp8 else 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
-    roof = dict(bound="mfma", achieved=round(ach, 2), peak=round(peak, 1), unit="TFLOP/s",
-                frac=round(ach / peak, 4), traffic=measured_traffic(w.name),
-                kernel="sparse_flash_fwd", algorithmic_flop=f_exact)
-    # the other kernels against their own rooflines
-    # pool: read Q, K, V; write the fp32 means, and for bf16 the transposed V tiles and the
-    # bf16 copies of the pooled keys and values
-    Mpad = (M + 63) // 64 * 64
-    pool_bytes = BH * (3 * w.N * w.d * es + (Mq + 2 * M) * w.d * 4)
-    if w.dtype == "bf16":
-        pool_bytes += BH * (w.N * w.d * 2 + 2 * Mpad * w.d * 2)
-    if "block_pool" in kern:
-        t = kern["block_pool"]["avg_ms"] * 1e-3
-        kern["block_pool"].update(bound="hbm", achieved_GBs=round(pool_bytes / t / 1e9, 1),
-                                  frac=round(pool_bytes / t / 1e9 / PEAK_HBM_GBS, 4))
-    if "block_score" in kern:
-        t = kern["block_score"]["avg_ms"] * 1e-3
-        fl = 2.0 * BH * Mq * M * w.d
-        kern["block_score"].update(bound="fp32", achieved_TFLOPs=round(fl / t / 1e12, 2),
-                                   frac=round(fl / t / 1e12 / PEAK_FP32_TFLOPS, 4))
-    if "block_select" in kern:
-        t = kern["block_select"]["avg_ms"] * 1e-3
-        by = BH * Mq * (M * 4 + 8 + (M + 63) // 64 * 64) + 4 * int(sel["kept_cnt"].sum())
-        kern["block_select"].update(bound="hbm", achieved_GBs=round(by / t / 1e9, 1),
-                                    frac=round(by / t / 1e9 / PEAK_HBM_GBS, 4))
-    if "extra_select" in kern:
-        t = kern["extra_select"]["avg_ms"] * 1e-3
-        fl = 2.0 * 2.0 * BH * Mq * w.N * w.d        # two bf16 passes (hi/lo split of q̄)
-        kern["extra_select"].update(bound="mfma", achieved_TFLOPs=round(fl / t / 1e12, 2),
-                                    frac=round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4))
-    kern["sparse_flash_fwd"].update(bound="mfma", achieved_TFLOPs=round(ach, 2),
-                                    frac=round(ach / peak, 4))
+    headline = None
+    if a.headline and a.config == 4 and not ov and not a.qk_fp8:
+        w5 = workload(5)
+        r5 = run_workload(w5, a, torch, sa, dev, a.headline_steps, 1)
+        roof5 = kernel_rooflines(w5, r5["kern"], r5["sel"], r5["call_stats"], False, peaks)
+        _, _, kf5 = selection_stats(r5["sel"], w5, w5.B, w5.H)
+        headline = dict(workload=w5.name, N=w5.N, H=w5.H, steps=a.headline_steps,
+                        ms_per_call=round(r5["ms_per_call"], 3),
+                        ms_per_call_median=round(float(np.median(r5["per_call"])), 3),
+                        roofline=roof5, kept_fraction=round(kf5, 4),
+                        exact_tflop=round(4.0 * w5.d * r5["call_stats"]["exact_pairs"] / 1e12, 4),
+                        kernels=r5["kern"], call_stats=r5["call_stats"])
 
-    cpu = None
+    cpu, check = None, None
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         t0 = time.perf_counter()
-        cpu = cpu_baseline(w, x, heads=tuple(range(min(4, w.H))), n_sparse=96, n_dense=24)
+        cpu, refs = cpu_baseline(w, r["x"], heads=tuple(range(min(4, w.H))), n_sparse=96, n_dense=24)
         log(f"[bench] oracle sample took {time.perf_counter() - t0:.1f} s")
+        check = selection_check(w, sel, refs)
 
+    ms_per_call = r["ms_per_call"]
+    per_call = r["per_call"]
     res = {
         "metric": "sol-attn fwd ms/call + MFMA util, N=65536 H=24 d=128 bf16 tau=1.3",
         "value": round(ms_per_call, 4),
@@ -331,6 +425,7 @@ def main():
                    "dense_rows": list(w.dense_rows)},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "measured_peaks": peaks,
         "effective_tflops": round(f_exact / (ms_per_call * 1e-3) / 1e12, 2),
         "mfma_util": round(f_exact / (ms_per_call * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kept_fraction": round(kept_frac, 4),
@@ -338,6 +433,8 @@ def main():
         "centroid_tflop": round(f_cent / 1e12, 4),
         "kernels": kern,
         "call_stats": call_stats,
+        "selection_check": check,
+        "headline": headline,
     }
     print(json.dumps(res), flush=True)
 

@@ -9,5 +9,5 @@ from ._lib import (  # noqa: F401
     SolattnError, Opts, WsLayout, Selection, lib, sol_attn, sol_attn_noalloc, sla_attn, local3d_attn, workspace_layout,
     workspace_bytes, workspace_bytes_any, free_default_workspaces, kept_masks,
     alloc_workspace, selection_views, status_string, last_error, kernel_names, timing_enable,
-    timing_read, make_opts, header_functions, pair_schedule, PAIR_STRIDES, NOALLOC_SCRATCH_BYTES,
+    timing_read, peak_probe, make_opts, header_functions, pair_schedule, PAIR_STRIDES, NOALLOC_SCRATCH_BYTES,
 )

@@ -119,6 +119,8 @@ def lib() -> ctypes.CDLL:
     L.solattn_timing_read.restype = i
     L.solattn_kernel_name.argtypes = [i]
     L.solattn_kernel_name.restype = ctypes.c_char_p
+    L.solattn_peak_probe.argtypes = [i, vp, ctypes.c_size_t, i, vp, ctypes.POINTER(ctypes.c_double)]
+    L.solattn_peak_probe.restype = i
     ip = ctypes.POINTER(ctypes.c_int)
     L.solattn_pair_schedule.argtypes = [i, i, i, i, ip, ip, i]
     L.solattn_pair_schedule.restype = i
@@ -201,6 +203,20 @@ def make_opts(dtype=BF16, strides=None, dense_rows=(0, 0), workspace=0, workspac
     if q_rows is not None:
         o.q_row_begin, o.q_row_end = int(q_rows[0]), int(q_rows[1])
     return o
+
+
+def peak_probe(kind: int, buf, iters: int = 1, stream=None) -> float:
+    """Launch one achievable-peak probe (solattn_peak_probe) on buf (a uint8 GPU tensor) and
+    return its work per launch (flop for kinds 0 and 1, bytes moved for kind 2)."""
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(buf.device).cuda_stream
+    work = ctypes.c_double()
+    rc = lib().solattn_peak_probe(int(kind), buf.data_ptr(), buf.numel() * buf.element_size(), int(iters),
+                                  stream, ctypes.byref(work))
+    if rc != OK:
+        raise SolattnError(rc, "peak probe")
+    return work.value
 
 
 def timing_enable(on: bool = True) -> None:

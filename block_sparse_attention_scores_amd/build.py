@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsolattn.so")
 SOURCES = ["api.cpp", "pool.hip", "score.hip", "select.hip", "extra.hip", "flash.hip", "stats.hip", "quant.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "probe.hip"]
 ARCH = os.environ.get("SOLATTN_ARCH", "gfx950")
 
 COMMON = [

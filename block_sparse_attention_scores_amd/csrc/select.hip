@@ -19,6 +19,9 @@
 // registers (RU per lane, M <= 64 RU), and every pass (mean, deviation, threshold or radix
 // select, compaction) works on them; rows longer than that are read once per pass.  All
 // reductions have a fixed order, so results are deterministic.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -46,17 +49,15 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // fixed-order wave reduction (deterministic).
 constexpr int SEL_ROWS = 4;
 
-// RU > 0: the row (M <= 64 * RU blocks) is held in registers, block 64u + lane in register u.
-// RU == 0: the row is read from memory on every pass (any M).
-template <int RU>
-__global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
-  extern __shared__ uint32_t nbm_all[];   // local 3-D mode: one neighbourhood bitmap (Mpad/32 words) per wave
-  __shared__ int hist_all[SEL_ROWS][256];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int i = blockIdx.x * SEL_ROWS + wv, bh = blockIdx.y;
-  if (i >= P.Mq) return;                   // the whole wave: nothing below waits for other waves
+// One row (query block i of problem bh) by one wave.  RU > 0: the row's scores arrive in
+// registers (rsv: block 64u + lane in register u, M <= 64 RU); RU == 0: the row is read from
+// memory on every pass (any M).  hist: this wave's 256-bin histogram; nbm: its local 3-D bitmap.
+// MODE: 0 sol, 1 sla, 2 local 3-D, -1 any (taken from P.mode at run time).
+template <int RU, int MODE>
+__device__ __forceinline__ void select_row(const Problem& P, int bh, int i, const float* rsv, int* hist,
+                                           uint32_t* nbm) {
+  const int mode = MODE >= 0 ? MODE : P.mode;
+  const int lane = threadIdx.x & 63;
   const int M = P.M, nu = (M + 63) >> 6, nw = P.Mpad >> 6;
   const size_t row = (size_t)bh * P.Mq + i;
   const float* s = P.scores + row * P.Mpad;
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
   const bool lists = P.keep_lists != 0;
 
   const bool dense = i >= P.dense_q0 && i < P.dense_q1;
-  if (dense || (P.mode == 0 && P.keep_all)) {
+  if (dense || (mode == 0 && P.keep_all)) {
     for (int wd = lane; wd < nw; wd += 64) {
       const int nb = M - 64 * wd;       // blocks of this word that exist
       bm[wd] = nb >= 64 ? ~0ull : (nb > 0 ? ((1ull << nb) - 1ull) : 0ull);
@@ -84,15 +85,8 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
   }
 
   // the row's scores: block 64u + lane (padding columns up to Mpad exist but are never used)
-  float sv[RU > 0 ? RU : 1];
-  if constexpr (RU > 0) {
-    if (P.mode != 2) {
-#pragma unroll
-      for (int u = 0; u < RU; ++u) sv[u] = u < nu ? s[64 * u + lane] : 0.f;
-    }
-  }
   auto score = [&](int u) -> float {
-    if constexpr (RU > 0) return sv[u];
+    if constexpr (RU > 0) return rsv[u];
     else return s[64 * u + lane];
   };
   // loop bound over the row's 64-block groups: a constant (unrolled, registers indexed
@@ -109,9 +103,8 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
   uint32_t kstar = 0;         // sla: key of the k-th largest non-forced score
   int need_eq = 0;            // sla: how many scores equal to kstar to take (lowest index first)
   bool sla_any = false;
-  uint32_t* nbm = nbm_all + (size_t)wv * (P.Mpad / 32);
 
-  if (P.mode == 0) {
+  if (mode == 0) {
     float acc = 0.f;
 #pragma unroll
     for (int u = 0; u < ulim; ++u)
@@ -127,7 +120,7 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
     const float var = wave_sum(acc2) / static_cast<float>(M);
     const float sd = sqrtf(var);
     theta = sd > 0.f ? fmaf(P.tau, sd, mu) : mu;
-  } else if (P.mode == 2) {
+  } else if (mode == 2) {
     // one lane per query token: mark the blocks of the token and of its grid neighbours
     for (int wd = lane; wd < P.Mpad / 32; wd += 64) nbm[wd] = 0u;
     wave_lds_sync();
@@ -155,7 +148,6 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
     int need = min(M - nforced, P.k_sla);
     sla_any = need > 0;
     if (sla_any) {
-      int* hist = hist_all[wv];
       uint32_t prefix = 0, pmask = 0;
       for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
@@ -219,9 +211,9 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
       if (j < M) {
         if (forced(j)) {
           keep = true;
-        } else if (P.mode == 0) {
+        } else if (mode == 0) {
           keep = score(u) > theta;
-        } else if (P.mode == 2) {
+        } else if (mode == 2) {
           keep = (nbm[j >> 5] >> (j & 31)) & 1u;
         } else if (sla_any) {
           const uint32_t key = float_key(score(u));
@@ -258,20 +250,162 @@ __global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
   }
 }
 
+// The sol row in registers, lean: per group of 64 blocks, a few per-lane compares and one ballot
+// give the bitmap word, which lane 0 parks in LDS (wbuf, 64 words per wave); the row's words go
+// out in one coalesced store at the end.  Only the last, partial group's deviation terms are
+// masked: rsv holds the row's scores with every padding position zero (see the loads below).
+template <int RU, bool LISTS>
+__device__ __forceinline__ void select_row_sol(const Problem& P, int bh, int i, const float* rsv,
+                                               uint64_t* wbuf) {
+  const int lane = threadIdx.x & 63;
+  const int M = P.M, nu = (M + 63) >> 6, nw = P.Mpad >> 6;
+  const size_t row = (size_t)bh * P.Mq + i;
+  uint64_t* bm = P.kept_bm + row * nw;
+  constexpr bool lists = LISTS;
+  const bool dense = i >= P.dense_q0 && i < P.dense_q1;
+  if (dense || P.keep_all) {
+    for (int wd = lane; wd < nw; wd += 64) {
+      const int nb = M - 64 * wd;
+      bm[wd] = nb >= 64 ? ~0ull : (nb > 0 ? ((1ull << nb) - 1ull) : 0ull);
+    }
+    if (lists)
+      for (int j = lane; j < P.Mpad; j += 64) {
+        if (j < M) P.kept_idx[row * M + j] = j;
+        P.mult[row * P.Mpad + j] = 0;
+      }
+    if (lane == 0) {
+      P.kept_cnt[row] = M;
+      P.extra_cnt[row] = 0;
+    }
+    return;
+  }
+  const int gi = i + P.q0;
+  const int diag_lo = (gi * P.bq) / P.bk;
+  const int diag_hi = min(M - 1, ((gi + 1) * P.bq - 1) / P.bk);
+  // mean (padding adds zeros), then the deviation over the M real blocks (two passes)
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < RU; ++u) acc += rsv[u];
+  const float mu = wave_sum(acc) / static_cast<float>(M);
+  float acc2 = 0.f;
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    const float dv = 64 * u + lane < M ? rsv[u] - mu : 0.f;
+    acc2 = fmaf(dv, dv, acc2);
+  }
+  const float sd = sqrtf(wave_sum(acc2) / static_cast<float>(M));
+  const float theta = sd > 0.f ? fmaf(P.tau, sd, mu) : mu;
+  int base = 0;
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    if (u < nu) {
+      const int j = 64 * u + lane;
+      const bool forced = j < P.sink_blocks || static_cast<unsigned>(j - diag_lo) <= static_cast<unsigned>(diag_hi - diag_lo);
+      const bool keep = j < M && (rsv[u] > theta || forced);
+      const uint64_t word = __ballot(keep);
+      if (lane == 0) wbuf[u] = word;
+      if (lists) {
+        if (keep) P.kept_idx[row * M + base + lanes_below(word)] = j;
+        if (j < M) P.mult[row * P.Mpad + j] = keep ? 0 : static_cast<uint8_t>(P.bk);
+      }
+      base += __popcll(word);
+    }
+  }
+  wave_lds_sync();
+  if (lane < nw) bm[lane] = lane < nu ? wbuf[lane] : 0ull;
+  wave_lds_sync();                          // the words are read before the next row's writes
+  if (lists)
+    for (int j = M + lane; j < P.Mpad; j += 64) P.mult[row * P.Mpad + j] = 0;
+  if (lane == 0) {
+    P.kept_cnt[row] = base;
+    P.extra_cnt[row] = 0;
+  }
+}
+
+// The pairing sums start from zero: the selection kernels clear them (any thread may, the plan
+// kernel runs after them on the stream).
+__device__ __forceinline__ void clear_pair_plan(const Problem& P) {
+  if (!P.pair_plan) return;
+  const int n = P.B * P.H * PAIR_STRIDES;
+  const int t = (blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+  const int nt = gridDim.x * gridDim.y * blockDim.x;
+  for (int e = t; e < n; e += nt) P.pair_plan[e] = 0;
+}
+
+// Generic rows (sla, and sol rows longer than 2048 blocks; M <= 64 RU): one wave per row, its
+// scores read once into registers.
+template <int RU, int MODE>
+__global__ __launch_bounds__(256) void block_select_reg_kernel(Problem P) {
+  __shared__ int hist_all[SEL_ROWS][256];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long r = (long)blockIdx.x * SEL_ROWS + wv;
+  clear_pair_plan(P);
+  if (r >= (long)P.B * P.H * P.Mq) return;
+  const int nu = (P.M + 63) >> 6;
+  const float* s = P.scores + r * P.Mpad;
+  float v[RU];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) v[u] = u < nu ? s[64 * u + lane] : 0.f;
+  select_row<RU, MODE>(P, static_cast<int>(r / P.Mq), static_cast<int>(r % P.Mq), v, hist_all[wv], nullptr);
+}
+
+// sol rows (M <= 64 RU): one wave per row, its scores read once into registers (padding zero),
+// the lean row routine above.  A wave that walked several rows would let the compiler keep every
+// group's lane conditions live across the walk (they do not change between rows), which costs
+// more than the walk saves.
+template <int RU, bool LISTS>
+__global__ __launch_bounds__(256) void block_select_sol_kernel(Problem P) {
+  __shared__ uint64_t wbuf_all[SEL_ROWS][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long r = (long)blockIdx.x * SEL_ROWS + wv;
+  clear_pair_plan(P);
+  if (r >= (long)P.B * P.H * P.Mq) return;
+  const int nu = (P.M + 63) >> 6;
+  const float* s = P.scores + r * P.Mpad;
+  float v[RU];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    v[u] = 0.f;
+    if (u < nu) {
+      const float x = s[64 * u + lane];
+      v[u] = 64 * u + lane < P.M ? x : 0.f;
+    }
+  }
+  select_row_sol<RU, LISTS>(P, static_cast<int>(r / P.Mq), static_cast<int>(r % P.Mq), v, wbuf_all[wv]);
+}
+
+// Memory path (the local 3-D pattern, and rows longer than 4096 blocks): one wave per row.
+__global__ __launch_bounds__(256) void block_select_kernel(Problem P) {
+  extern __shared__ uint32_t nbm_all[];   // local 3-D mode: one neighbourhood bitmap (Mpad/32 words) per wave
+  __shared__ int hist_all[SEL_ROWS][256];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = blockIdx.x * SEL_ROWS + wv, bh = blockIdx.y;
+  clear_pair_plan(P);
+  if (i >= P.Mq) return;                   // the whole wave: nothing below waits for other waves
+  select_row<0, -1>(P, bh, i, nullptr, hist_all[wv], nbm_all + (size_t)wv * (P.Mpad / 32));
+}
+
 // The tile steps a head's pairs of query blocks would take under pairing stride
-// s = blockIdx.y + 1: the kept-block union of each pair, summed (one workgroup per head and
-// stride; the threads stride over the (pair, bitmap word) index space, so that every lane
-// issues its own independent loads).
+// s = blockIdx.y + 1: the kept-block union of each pair, summed.  Workgroups (head, stride,
+// chunk of pairs); the threads stride over the chunk's (pair, bitmap word) index space, so that
+// every lane issues its own independent loads, and each workgroup adds its integer sum into the
+// head's total (zeroed by the selection kernel before it; integer sums do not depend on order).
+constexpr int PLAN_CHUNKS = 8;
+
 __global__ __launch_bounds__(256) void pair_plan_kernel(Problem P) {
-  const int bh = blockIdx.x, s = blockIdx.y + 1;
+  const int bh = blockIdx.x, s = blockIdx.y + 1, chunk = blockIdx.z;
   const int nd = P.dense_q1 - P.dense_q0, Ms = P.Mq - nd, npair = (Ms + 1) / 2;
   const int nw = P.Mpad / 64;
   const uint64_t* bm = P.kept_bm + (size_t)bh * P.Mq * nw;
-  const int total = npair * nw;
+  const int per = (npair + PLAN_CHUNKS - 1) / PLAN_CHUNKS;
+  const int p0 = chunk * per, p1 = min(npair, p0 + per);
+  const int total = max(0, p1 - p0) * nw;
   int acc = 0;
 #pragma unroll 4
   for (int e = threadIdx.x; e < total; e += 256) {
-    const int p = e / nw, w = e - p * nw;
+    const int p = p0 + e / nw, w = e % nw;
     int a, b;
     sparse_pair(p, s, Ms, P.dense_q0, nd, &a, &b);
     uint64_t x = bm[(size_t)a * nw + w];
@@ -283,27 +417,42 @@ __global__ __launch_bounds__(256) void pair_plan_kernel(Problem P) {
   __shared__ int part[4];
   if (threadIdx.x % 64 == 0) part[threadIdx.x / 64] = acc;
   __syncthreads();
-  if (threadIdx.x == 0)
-    P.pair_plan[(size_t)bh * PAIR_STRIDES + blockIdx.y] =
-        (long long)part[0] + part[1] + part[2] + part[3];
+  if (threadIdx.x == 0 && total > 0)
+    atomicAdd(reinterpret_cast<unsigned long long*>(P.pair_plan + (size_t)bh * PAIR_STRIDES + blockIdx.y),
+              static_cast<unsigned long long>(part[0] + part[1] + part[2] + part[3]));
 }
 
 hipError_t launch_pair_plan(const Problem& P, hipStream_t stream) {
   if (!P.pair_plan) return hipSuccess;
-  hipLaunchKernelGGL(pair_plan_kernel, dim3(P.B * P.H, PAIR_STRIDES), dim3(256), 0, stream, P);
+  hipLaunchKernelGGL(pair_plan_kernel, dim3(P.B * P.H, PAIR_STRIDES, PLAN_CHUNKS), dim3(256), 0, stream, P);
   return hipGetLastError();
 }
 
 hipError_t launch_block_select(const Problem& P, hipStream_t stream) {
   dim3 grid((P.Mq + SEL_ROWS - 1) / SEL_ROWS, P.B * P.H);
   const size_t lds = P.mode == 2 ? (size_t)SEL_ROWS * (P.Mpad / 32) * 4 : 0;
-  // registers for the row: the smallest instance that holds it
-  if (P.mode == 2 || P.M > 64 * 64)
-    hipLaunchKernelGGL(block_select_kernel<0>, grid, dim3(256), lds, stream, P);
-  else if (P.M <= 64 * 16)
-    hipLaunchKernelGGL(block_select_kernel<16>, grid, dim3(256), lds, stream, P);
-  else
-    hipLaunchKernelGGL(block_select_kernel<64>, grid, dim3(256), lds, stream, P);
+  if (P.mode == 2 || P.M > 64 * 64) {
+    hipLaunchKernelGGL(block_select_kernel, grid, dim3(256), lds, stream, P);
+    return hipGetLastError();
+  }
+  // registers for the row: the smallest instance that holds it, one wave per row
+  const long rows = (long)P.B * P.H * P.Mq;
+  const int wgs = static_cast<int>((rows + SEL_ROWS - 1) / SEL_ROWS);
+  auto go = [&](auto ru) {
+    constexpr int RU = decltype(ru)::value;
+    if (P.mode == 0 && RU <= 32) {
+      constexpr int R = RU <= 32 ? RU : 32;
+      if (!P.keep_lists) hipLaunchKernelGGL((block_select_sol_kernel<R, false>), dim3(wgs), dim3(256), 0, stream, P);
+      else hipLaunchKernelGGL((block_select_sol_kernel<R, true>), dim3(wgs), dim3(256), 0, stream, P);
+    } else if (P.mode == 0) {
+      hipLaunchKernelGGL((block_select_reg_kernel<RU, 0>), dim3(wgs), dim3(256), 0, stream, P);
+    } else {
+      hipLaunchKernelGGL((block_select_reg_kernel<RU, 1>), dim3(wgs), dim3(256), 0, stream, P);
+    }
+  };
+  if (P.M <= 64 * 16) go(std::integral_constant<int, 16>{});
+  else if (P.M <= 64 * 32) go(std::integral_constant<int, 32>{});
+  else go(std::integral_constant<int, 64>{});
   return hipGetLastError();
 }
 

@@ -380,6 +380,19 @@ int solattn_timing_enable(int enable);
 int solattn_timing_read(double* ms, long long* launches, int n);
 const char* solattn_kernel_name(int index);
 
+/*
+ * Achievable-peak probes (measurement aid; not part of the attention).  Launches one probe on
+ * `stream` (hipStream_t, NULL = null stream) and writes the work it does per launch to
+ * *work_per_launch; the caller times the launch (e.g. with events) to get the rate:
+ *   kind 0: bf16 32x32x16 matrix instructions in a loop, no memory (work: flop)
+ *   kind 1: fp32 32x32x2 matrix instructions in a loop (work: flop)
+ *   kind 2: copy of the first half of buf to its second half (work: bytes read + written)
+ * buf: device memory, 16-byte aligned, at least 2 MiB for kinds 0 and 1 (results that are
+ * never stored unless a sum hits one exact value); iters: loop trips for kinds 0 and 1 (>= 1).
+ * Returns SOLATTN_OK, SOLATTN_EINVAL or SOLATTN_EHIP.
+ */
+int solattn_peak_probe(int kind, void* buf, size_t bytes, int iters, void* stream, double* work_per_launch);
+
 #ifdef __cplusplus
 }
 #endif
