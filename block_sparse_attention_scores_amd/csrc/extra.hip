@@ -3,11 +3,12 @@
 // docs, common inputs table, extra_tokens row: extra high-score tokens each query block
 // attends beyond its selected blocks).
 //
-// Pass 1 keeps, per query block, every key whose score reaches a running threshold, in
-// candidate lists in the workspace.  The threshold starts from a seed taken from a sample of
-// the keys and rises whenever a list is cut back to its E best entries (by radix selection on
-// (score, token)): any list's E-th best is a lower bound of the final E-th best, so no key of
-// the final selection is ever dropped.
+// Pass 1 keeps, per query block, every key whose score reaches a threshold, in candidate lists
+// in the workspace.  The sampled pass (16-bit tensors) holds the threshold at a seed taken from
+// a sample of the keys and sends a query block whose lists could overflow to the exact pass;
+// the exact pass and the fp32 pass raise the threshold whenever a list is cut back to its E best
+// entries (by radix selection on (score, token)): any list's E-th best is a lower bound of the
+// final E-th best, so no key of the final selection is ever dropped.
 //   16-bit tensors (extra_seed_kernel, extra_tile_kernel): scores come from the 32x32x16 bf16
 //   matrix instruction with q̄ split into two bf16 parts (hi + lo), accurate to ~2^-17
 //   relative (fp32-like), while the keys are exact bf16; a workgroup owns 128 query blocks and
@@ -36,6 +37,10 @@ constexpr int XR = EXTRA_GROUP_F32;   // query blocks per workgroup (fp32 first 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int XSTEP = 32;   // tokens per wave step
+
+// Fill of a candidate list of the 16-bit sampled pass one of whose halves could have
+// overflowed (its query block goes to the exact pass).
+constexpr int EXTRA_PART_OVERFLOW = -1;
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -468,6 +473,14 @@ struct FlagCopy {
   }
 };
 
+// float -> bfloat16 bits, round to nearest even, NaN kept a NaN; both results are computed and
+// one selected, so a loop of these has no branch.
+__device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : r);
+}
+
 // The per-lane part shared by the two kernels: q̄ split into bf16 hi + lo fragments for this
 // lane's query block (zero past the last one), the tile loader and the score products.
 template <int D>
@@ -478,16 +491,28 @@ struct ExtraTiles {
   uint32_t ak;                                         // lane's A-fragment byte offset in a 32-row step
   uint32_t ksn_b;
 
+  // row: a valid row of qbar (callers clamp it); has_row = false zeroes the fragments.  The
+  // loads are unconditional 16-byte loads, all in flight together, and the conversion has no
+  // branch, so the set-up costs one memory round trip.
   __device__ void init(const Problem& P, size_t row, bool has_row) {
     const float* qb = P.qbar + row * D;
     const int l = threadIdx.x & 63;
+    float4 x4[D / 8];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const float4* src = reinterpret_cast<const float4*>(qb + 16 * ks + 8 * (l / 32));
+      x4[2 * ks] = src[0];
+      x4[2 * ks + 1] = src[1];
+    }
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = has_row ? qb[16 * ks + 8 * (l / 32) + e] : 0.f;
-        const uint16_t hb = f32_to_bf16(x);
-        const uint16_t lb = f32_to_bf16(x - bf16_to_f32(hb));
+        const float4 v = x4[2 * ks + e / 4];
+        const float c = (e % 4 == 0) ? v.x : (e % 4 == 1) ? v.y : (e % 4 == 2) ? v.z : v.w;
+        const float x = has_row ? c : 0.f;
+        const uint16_t hb = bf16_bits_rne(x);
+        const uint16_t lb = bf16_bits_rne(x - bf16_to_f32(hb));
         qhi[ks][e] = __builtin_bit_cast(__bf16, hb);
         qlo[ks][e] = __builtin_bit_cast(__bf16, lb);
       }
@@ -659,10 +684,18 @@ __device__ __forceinline__ float key_threshold(uint32_t thr) {
   return thr == 0u ? -__builtin_inff() : key_float(thr);
 }
 
-// repair = 0: every sparse query block from its seed; repair = 1: only the query blocks the
-// merge flagged, from the lowest threshold (every candidate competes: the exact selection).
-template <int D>
-__global__ __launch_bounds__(256, 2) void extra_tile_kernel(Problem P, int repair) {
+// REPAIR = false: the sampled pass, every sparse query block from its seed.  The threshold never
+// changes, so there is no cut: lanes l and l+32 (the two halves of a query block's 32-token
+// step) append to interleaved slots of the (query block, slice) list, lane l to slots 2k and
+// lane l+32 to slots 2k+1, and at the end the longer lane closes the gaps after the shorter
+// one's last entry.  A lane that could overflow its half of the list stops appending and the
+// list's fill is marked EXTRA_PART_OVERFLOW, which sends the query block to the exact pass.
+// REPAIR = true: only the query blocks the merge flagged, from the lowest threshold (every
+// candidate competes: the exact selection), one list per (query block, slice) cut back to its
+// best E whenever the next step could overflow it.
+template <int D, bool REPAIR>
+__global__ __launch_bounds__(256, 2) void extra_tile_kernel(Problem P) {
+  constexpr bool repair = REPAIR;
   __shared__ ExtraSmem<D> sm;
   using TT = ExtraTiles<D>;
   const int E = P.extra, N = P.N, S = P.extra_slices, nl = P.extra_lists;
@@ -726,82 +759,158 @@ __global__ __launch_bounds__(256, 2) void extra_tile_kernel(Problem P, int repai
   const uint32_t my_off = (uint32_t)rl * row_stride;
   int cnt = 0;
 
-  // Append the candidates (bits) of one 32-token step starting at token tw (scores c): lane l
-  // first, then its partner l+32, each in register order; then cut the lists that the next
-  // step could overflow.
-  auto append = [&](const f32x16_t& c, uint32_t bits, int tw) {
-    if (__ballot(bits != 0) == 0) return;
-    const int mine = __popc(bits);
-    const int other = __shfl_xor(mine, 32);
-    uint32_t addr = my_off + static_cast<uint32_t>(cnt + (l < 32 ? 0 : other)) * 8u;
-    cnt += mine + other;
-    const uint32_t tk0 = static_cast<uint32_t>(tw + (l / 32) * 4);
+  if constexpr (!REPAIR) {
+    // Sampled pass.  Lane l's k-th candidate goes to slot 2k + l/32 of its list.
+    constexpr int HALF = EXTRA_CAP / 2;
+    uint32_t addr = my_off + static_cast<uint32_t>(l / 32) * 8u;
+    bool full = false;                            // this lane's half could overflow: stop
+    auto append = [&](const f32x16_t& c, bool on, int tw) {
+      if (__ballot(on) == 0) return;
+      const uint32_t tk0 = static_cast<uint32_t>(tw + (l / 32) * 4);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint32_t bit = (bits >> r) & 1u;
-      if (bit) {
-        u32x2 v2;
-        v2.x = __float_as_uint(c[r]);
-        v2.y = tk0 + static_cast<uint32_t>((r / 4) * 8 + (r % 4));
-        __builtin_amdgcn_raw_buffer_store_b64(v2, brsrc, addr, 0, 0);
-      }
-      addr += bit << 3;
-    }
-    uint64_t m = __ballot(l < 32 && cnt > EXTRA_CAP - XSTEP);
-    if (m) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this wave's stores, visible
-      while (m) {
-        const int rr = __builtin_ctzll(m);
-        m &= m - 1;
-        uint2* rb = P.extra_buf + (((size_t)bh * P.Mq + i0w + rr) * nl + slice) * EXTRA_CAP;
-        const int crr = __shfl(cnt, rr);
-        const uint32_t kth = wave_cut(rb, crr, E, sm.hist[w], sm.scr[w]);
-        if (rl == rr) {
-          thr = max(thr, kth);
-          tf = key_threshold(thr);
-          cnt = E;
+      for (int r = 0; r < 16; ++r) {
+        if (on && c[r] >= tf) {
+          u32x2 v2;
+          v2.x = __float_as_uint(c[r]);
+          v2.y = tk0 + static_cast<uint32_t>((r / 4) * 8 + (r % 4));
+          __builtin_amdgcn_raw_buffer_store_b64(v2, brsrc, addr, 0, 0);
+          addr += 16u;
         }
-        wave_sync();
+      }
+    };
+    for (int it = 0; it < XNB - 1 && it < ntile; ++it) issue(it);
+    // the previous tile's scores, stored one tile late
+    f32x16_t pc0 = {}, pc1 = {};
+    bool pon = false;
+    int ptw = 0;
+#pragma unroll 1
+    for (int it = 0; it < ntile; ++it) {
+      const int t0 = t_lo + it * XTOK, j = t0 >> 6;
+      wait_tiles<OPS>(min(XNB - 2, ntile - 1 - it));
+      tile_barrier();
+      const bool cand = row_ok && j < P.M && !FlagCopy::kept(sm.fl[it % XNB][0], j);
+      // every wave has read this tile's flags before its buffer is refilled (a tile later)
+      if (it + XNB - 1 < ntile) issue(it + XNB - 1);
+      append(pc0, pon, ptw);
+      append(pc1, pon, ptw + 32);
+      // the next tile appends at most 32 entries per lane
+      full = full || (addr - my_off) > static_cast<uint32_t>(2 * (HALF - 2 * 16)) * 8u;
+      pon = false;
+      if (wave_on && __ballot(cand) != 0) {
+        pc0 = T.scores(sm.k[it % XNB], 0);
+        pc1 = T.scores(sm.k[it % XNB], 1);
+        pon = cand && !full;
+        ptw = t0;
       }
     }
-  };
-  auto cand_bits = [&](const f32x16_t& c) {
-    uint32_t bits = 0;
-#pragma unroll
-    for (int r = 15; r >= 0; --r) bits = bits * 2u + (c[r] >= tf ? 1u : 0u);
-    return bits;
-  };
-
-  for (int it = 0; it < XNB - 1 && it < ntile; ++it) issue(it);
-  // the previous tile's scores and candidate bits, stored one tile late
-  f32x16_t pc0 = {}, pc1 = {};
-  uint32_t pb0 = 0, pb1 = 0;
-  int ptw = 0;
+    append(pc0, pon, ptw);
+    append(pc1, pon, ptw + 32);
+    // Close the gaps: slots [0, 2m) hold both lanes' first m = min(count, partner's count)
+    // entries; the longer lane moves its remaining entries (slots 2k + l/32, k >= m) down to
+    // slots 2m, 2m + 1, ... in order, so the list is contiguous.  A slot is only written after
+    // it was read (destination 2m + t <= source 2(m + t) + l/32), and the reads bypass the
+    // vector cache (glc) after this lane's own stores completed.
+    cnt = static_cast<int>((addr - my_off) >> 4);
+    const int ocnt = __shfl_xor(cnt, 32);
+    const bool ofull = __shfl_xor(full ? 1 : 0, 32) != 0;
+    if (!full && !ofull && cnt > ocnt) {
+      __builtin_amdgcn_s_waitcnt(0);
+      const uint32_t h = static_cast<uint32_t>(l / 32);
 #pragma unroll 1
-  for (int it = 0; it < ntile; ++it) {
-    const int t0 = t_lo + it * XTOK, j = t0 >> 6;
-    wait_tiles<OPS>(min(XNB - 2, ntile - 1 - it));
-    tile_barrier();
-    const bool cand = row_ok && j < P.M && !FlagCopy::kept(sm.fl[it % XNB][0], j);
-    // every wave has read this tile's flags before its buffer is refilled (a tile later)
-    if (it + XNB - 1 < ntile) issue(it + XNB - 1);
+      for (int k0 = ocnt; k0 < cnt; k0 += 8) {
+        u32x2 e[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (k0 + t < cnt)
+            e[t] = __builtin_amdgcn_raw_buffer_load_b64(
+                brsrc, my_off + (2u * static_cast<uint32_t>(k0 + t) + h) * 8u, 0, 1);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (k0 + t < cnt)
+            __builtin_amdgcn_raw_buffer_store_b64(
+                e[t], brsrc, my_off + static_cast<uint32_t>(ocnt + k0 + t) * 8u, 0, 0);
+      }
+    }
+    if (l < 32 && i < P.Mq)
+      P.extra_part[row * nl + slice] = (full || ofull) ? EXTRA_PART_OVERFLOW : cnt + ocnt;
+  } else {
+    // Exact pass.  Append the candidates (bits) of one 32-token step starting at token tw
+    // (scores c): lane l first, then its partner l+32, each in register order; then cut the
+    // lists that the next step could overflow.
+    auto append = [&](const f32x16_t& c, uint32_t bits, int tw) {
+      if (__ballot(bits != 0) == 0) return;
+      const int mine = __popc(bits);
+      const int other = __shfl_xor(mine, 32);
+      uint32_t addr = my_off + static_cast<uint32_t>(cnt + (l < 32 ? 0 : other)) * 8u;
+      cnt += mine + other;
+      const uint32_t tk0 = static_cast<uint32_t>(tw + (l / 32) * 4);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t bit = (bits >> r) & 1u;
+        if (bit) {
+          u32x2 v2;
+          v2.x = __float_as_uint(c[r]);
+          v2.y = tk0 + static_cast<uint32_t>((r / 4) * 8 + (r % 4));
+          __builtin_amdgcn_raw_buffer_store_b64(v2, brsrc, addr, 0, 0);
+        }
+        addr += bit << 3;
+      }
+      uint64_t m = __ballot(l < 32 && cnt > EXTRA_CAP - XSTEP);
+      if (m) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this wave's stores, visible
+        while (m) {
+          const int rr = __builtin_ctzll(m);
+          m &= m - 1;
+          uint2* rb = P.extra_buf + (((size_t)bh * P.Mq + i0w + rr) * nl + slice) * EXTRA_CAP;
+          const int crr = __shfl(cnt, rr);
+          const uint32_t kth = wave_cut(rb, crr, E, sm.hist[w], sm.scr[w]);
+          if (rl == rr) {
+            thr = max(thr, kth);
+            tf = key_threshold(thr);
+            cnt = E;
+          }
+          wave_sync();
+        }
+      }
+    };
+    auto cand_bits = [&](const f32x16_t& c) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int r = 15; r >= 0; --r) bits = bits * 2u + (c[r] >= tf ? 1u : 0u);
+      return bits;
+    };
+
+    for (int it = 0; it < XNB - 1 && it < ntile; ++it) issue(it);
+    // the previous tile's scores and candidate bits, stored one tile late
+    f32x16_t pc0 = {}, pc1 = {};
+    uint32_t pb0 = 0, pb1 = 0;
+    int ptw = 0;
+#pragma unroll 1
+    for (int it = 0; it < ntile; ++it) {
+      const int t0 = t_lo + it * XTOK, j = t0 >> 6;
+      wait_tiles<OPS>(min(XNB - 2, ntile - 1 - it));
+      tile_barrier();
+      const bool cand = row_ok && j < P.M && !FlagCopy::kept(sm.fl[it % XNB][0], j);
+      // every wave has read this tile's flags before its buffer is refilled (a tile later)
+      if (it + XNB - 1 < ntile) issue(it + XNB - 1);
+      append(pc0, pb0, ptw);
+      append(pc1, pb1, ptw + 32);
+      pb0 = pb1 = 0;
+      if (wave_on && __ballot(cand) != 0) {
+        pc0 = T.scores(sm.k[it % XNB], 0);
+        pc1 = T.scores(sm.k[it % XNB], 1);
+        if (cand) {
+          pb0 = cand_bits(pc0);
+          pb1 = cand_bits(pc1);
+        }
+        ptw = t0;
+      }
+    }
     append(pc0, pb0, ptw);
     append(pc1, pb1, ptw + 32);
-    pb0 = pb1 = 0;
-    if (wave_on && __ballot(cand) != 0) {
-      pc0 = T.scores(sm.k[it % XNB], 0);
-      pc1 = T.scores(sm.k[it % XNB], 1);
-      if (cand) {
-        pb0 = cand_bits(pc0);
-        pb1 = cand_bits(pc1);
-      }
-      ptw = t0;
-    }
+    // publish the list lengths of the flagged query blocks
+    if (l < 32 && i < P.Mq && row_ok) P.extra_part[row * nl + slice] = cnt;
   }
-  append(pc0, pb0, ptw);
-  append(pc1, pb1, ptw + 32);
-  // publish the list lengths (in the repair pass only for the flagged query blocks)
-  if (l < 32 && i < P.Mq && (!repair || row_ok)) P.extra_part[row * nl + slice] = cnt;
 }
 
 // Pass 2: best E of the 4*S partial lists of one query block, ranked by token.  The lists stay
@@ -872,17 +981,20 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) 
   if (repair && P.extra_flag[row] == 0) return;
   int cnts[16];
   int total = 0;
+  bool overflow = false;
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
-    cnts[q] = q < nl ? part[q] : 0;
+    const int f = q < nl ? part[q] : 0;
+    overflow = overflow || f == EXTRA_PART_OVERFLOW;
+    cnts[q] = f == EXTRA_PART_OVERFLOW ? 0 : f;
     total += cnts[q];
   }
   if (!repair) {
-    // every candidate scoring at or above the seeded threshold is in the lists (or was cut in
-    // favour of better ones); fewer than min(E, |candidates|) of them means the seed was too
-    // high, and the query block goes to the exact repair pass
+    // every candidate scoring at or above the seeded threshold is in the lists; fewer than
+    // min(E, |candidates|) of them means the seed was too high, and a list that could have
+    // overflowed may have lost some: either way the query block goes to the exact repair pass
     const int ncand = P.N - P.bk * P.kept_cnt[row];
-    const bool short_ = total < min(E, ncand);
+    const bool short_ = overflow || total < min(E, ncand);
     if (l == 0) P.extra_flag[row] = short_ ? 1 : 0;
     if (short_) return;
   }
@@ -985,31 +1097,48 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) 
   wave_sync();
   // survivors are in toks[0..c): sort them ascending, write them out, and take them out of
   // their key blocks' centroid terms (key blocks are 64 tokens: block_k is 64 in this library).
-  // In the register paths the survivors keep the order of the lists, which is ascending except
-  // inside one 32-token step (a lane's tokens, then its partner's); an odd-even transposition
-  // sort, run until a whole round swaps nothing, takes a few rounds there (and stays exact for
-  // any order).
+  // In the register paths the survivors keep the order of the lists: slices in order, and
+  // inside a list either a lane's tokens then its partner's per 32-token step (exact pass) or
+  // the two lanes' ascending runs interleaved entry by entry, the longer run's rest after them
+  // (sampled pass), so every token sits near its sorted place.  An odd-even transposition sort,
+  // run until a whole round swaps nothing, takes few rounds there (and stays exact for any
+  // order); it runs in registers, four entries per lane, a round being a few instructions and
+  // two lane shifts.
   const int c = scr[3];
   wave_sync();
+  {
+    // the sort runs in registers: entry 4l + e in v[e] of lane l (past c: INT_MAX, which stays
+    // at the end); a round compares the even pairs (4l, 4l+1), (4l+2, 4l+3), then the odd pairs
+    // (4l+1, 4l+2) and (4l+3, 4l+4), the last across the lane boundary
+    static_assert(MAX_EXTRA == 4 * 64, "four entries per lane");
+    int v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = 4 * l + e < c ? toks[4 * l + e] : 0x7FFFFFFF;
+    auto cswap = [](int& a, int& b, bool& sw) {
+      const int lo = min(a, b), hi = max(a, b);
+      sw = sw || lo != a;
+      a = lo;
+      b = hi;
+    };
 #pragma unroll 1
-  for (;;) {
-    bool swapped = false;
-#pragma unroll
-    for (int ph = 0; ph < 2; ++ph) {
-#pragma unroll
-      for (int p = 2 * l + ph; p < MAX_EXTRA; p += 128) {
-        if (p + 1 < c) {
-          const int x = toks[p], y = toks[p + 1];
-          if (x > y) {
-            toks[p] = y;
-            toks[p + 1] = x;
-            swapped = true;
-          }
-        }
+    for (;;) {
+      bool sw = false;
+      cswap(v[0], v[1], sw);
+      cswap(v[2], v[3], sw);
+      cswap(v[1], v[2], sw);
+      const int next0 = __shfl_down(v[0], 1);          // lane l+1's first entry
+      const int prev3 = __shfl_up(v[3], 1);            // lane l-1's last entry
+      if (l < 63 && next0 < v[3]) {
+        v[3] = next0;
+        sw = true;
       }
-      wave_sync();
+      if (l > 0) v[0] = max(v[0], prev3);
+      if (__ballot(sw) == 0) break;
     }
-    if (__ballot(swapped) == 0) break;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * l + e < c) toks[4 * l + e] = v[e];
+    wave_sync();
   }
   int* out = P.extra_idx + row * MAX_EXTRA;
   uint8_t* mr = P.mult + row * P.Mpad;
@@ -1037,8 +1166,13 @@ hipError_t launch_extra_select(const Problem& P, hipStream_t stream) {
         if (P.d == 128) hipLaunchKernelGGL(extra_seed_kernel<128>, gseed, dim3(256), 0, stream, P);
         else hipLaunchKernelGGL(extra_seed_kernel<64>, gseed, dim3(256), 0, stream, P);
       }
-      if (P.d == 128) hipLaunchKernelGGL(extra_tile_kernel<128>, g16, dim3(256), 0, stream, P, repair);
-      else hipLaunchKernelGGL(extra_tile_kernel<64>, g16, dim3(256), 0, stream, P, repair);
+      if (repair) {
+        if (P.d == 128) hipLaunchKernelGGL((extra_tile_kernel<128, true>), g16, dim3(256), 0, stream, P);
+        else hipLaunchKernelGGL((extra_tile_kernel<64, true>), g16, dim3(256), 0, stream, P);
+      } else {
+        if (P.d == 128) hipLaunchKernelGGL((extra_tile_kernel<128, false>), g16, dim3(256), 0, stream, P);
+        else hipLaunchKernelGGL((extra_tile_kernel<64, false>), g16, dim3(256), 0, stream, P);
+      }
     } else {
       if (P.d == 128) hipLaunchKernelGGL(extra_select_kernel<128>, grid, dim3(256), 0, stream, P, repair);
       else hipLaunchKernelGGL(extra_select_kernel<64>, grid, dim3(256), 0, stream, P, repair);

@@ -241,6 +241,39 @@ def test_extra_selection_exact_pass(flags):
     assert (sel["extra_cnt"] == 256).all()
 
 
+def test_extra_selection_overflow_goes_to_exact_pass():
+    # The opposite failure of the seed: every key block the seed's sample reads scores far below
+    # the rest, so the seed admits nearly every token and the sampled pass's lists would
+    # overflow.  Such query blocks must be flagged and selected again by the exact pass; the
+    # selection must still be the oracle's.  The sample here is the first 32 tokens of key block
+    # 8s + (37 s mod 8) for run s of 64 (N = 32768: 512 key blocks, 64 runs); whole blocks are
+    # lowered so the construction does not depend on the run's half.
+    B, H, N, d = 1, 2, 32768, 128
+    M = N // 64
+    runs = 64
+    sampled = {(s * M) // runs + (s * 37) % (M // runs) for s in range(runs)}
+    rng = np.random.default_rng([11, 5])
+    u = rng.standard_normal(d).astype(np.float32)
+    u /= np.linalg.norm(u)
+    q = rng.standard_normal((B, H, N, d), dtype=np.float32) + 2.0 * u
+    k = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    low = np.zeros(N, dtype=bool)
+    for j in sampled:
+        low[64 * j:64 * j + 64] = True
+    k[:, :, ~low, :] += 3.0 * u
+    v = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    bits = [bf16_round(a) for a in (q, k, v)]
+    w = Workload(0, "overflow", B=B, H=H, T=1, Hh=1, Ww=N, d=d, dtype="bf16", mode="sol",
+                 block_q=64, block_k=64, tau=1.3, extra_tokens=256, sink_range=64)
+    x = Inputs(w, tuple(range(H)), *[bf16_to_f32(b) for b in bits], *bits)
+    _, sel, rep = run_and_check(w, x, range(H), qblocks=[0, 1, 63, 200, 257, 400, 511])
+    assert rep.extra_flips == 0
+    flagged = int((sel["extra_flag"] == 1).sum())
+    print(f"[overflow] query blocks sent to the exact pass: {flagged} of {sel['extra_flag'].size}", flush=True)
+    assert flagged > 0
+    assert (sel["extra_cnt"] == 256).all()
+
+
 def test_batch_and_dense_rows_fp32():
     x = random_qkv(2, 2, 4096, 64, seed=9, dtype="fp32")
     w = workload(1, B=2, dense_rows=(3072, 4096), extra_tokens=64, sink_range=100)
