@@ -133,9 +133,9 @@ constexpr int EXTRA_GROUP_F32 = 32;
 // Token slices of the extra-token selection and candidate lists per query block.  fp32: enough
 // slices for about 1536 workgroups (at most 4), one list per slice and wave.  16-bit: the slice
 // count (at most 16) whose workgroups fill the last of their rounds best (EXTRA_SLOTS resident
-// at a time: two per compute unit of the 256), preferring fewer slices on near ties; one list per
-// slice.
-constexpr int EXTRA_SLOTS = 512;
+// at a time: three per compute unit of the 256), preferring fewer slices on near ties; one list
+// per slice.
+constexpr int EXTRA_SLOTS = 768;
 __host__ __device__ inline void extra_split(bool f32, int B, int H, int Mq, int* slices, int* lists) {
   if (f32) {
     const long groups = (long)((Mq + EXTRA_GROUP_F32 - 1) / EXTRA_GROUP_F32) * B * H;

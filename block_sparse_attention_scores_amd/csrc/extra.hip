@@ -429,6 +429,16 @@ struct ExtraSmem {
   int any;
 };
 
+// The sampled pass: three tile buffers (two tiles in flight), one flag run per tile and no cut
+// scratch, so that three workgroups fit in a compute unit's LDS.
+constexpr int XNB_S = 3;
+template <int D>
+struct ExtraSampledSmem {
+  uint16_t k[XNB_S][XTOK * D];
+  uint32_t fl[XNB_S][1][256];
+  int any;
+};
+
 // Barrier for the tile loop: every wave has waited for its own copies of the tile (vmcnt), so
 // after it the whole tile is in LDS; the memory clobber keeps LDS accesses on their side.  No
 // memory fence: a fence would wait for every outstanding copy, including the later tiles'.
@@ -694,9 +704,10 @@ __device__ __forceinline__ float key_threshold(uint32_t thr) {
 // candidate competes: the exact selection), one list per (query block, slice) cut back to its
 // best E whenever the next step could overflow it.
 template <int D, bool REPAIR>
-__global__ __launch_bounds__(256, 2) void extra_tile_kernel(Problem P) {
+__global__ __launch_bounds__(256, REPAIR ? 2 : 3) void extra_tile_kernel(Problem P) {
   constexpr bool repair = REPAIR;
-  __shared__ ExtraSmem<D> sm;
+  constexpr int NB = REPAIR ? XNB : XNB_S;             // tile buffers
+  __shared__ std::conditional_t<REPAIR, ExtraSmem<D>, ExtraSampledSmem<D>> sm;
   using TT = ExtraTiles<D>;
   const int E = P.extra, N = P.N, S = P.extra_slices, nl = P.extra_lists;
   int unit, grp;                                 // unit = (head, slice)
@@ -743,10 +754,10 @@ __global__ __launch_bounds__(256, 2) void extra_tile_kernel(Problem P) {
   auto issue = [&](int it) {
     const int t0 = t_lo + it * XTOK;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + (int64_t)t0 * P.k.sn, 64u * ksn_b);
-    char* kd = reinterpret_cast<char*>(sm.k[it % XNB]);
+    char* kd = reinterpret_cast<char*>(sm.k[it % NB]);
 #pragma unroll
     for (int u = 0; u < TT::PT; ++u) buf_to_lds16(krs, kvoff[u], kd + (u * 4 + w) * 1024);
-    buf_to_lds4s(frs, fvoff, static_cast<uint32_t>(t0 >> 11) * 4u, sm.fl[it % XNB][0] + 64 * w);
+    buf_to_lds4s(frs, fvoff, static_cast<uint32_t>(t0 >> 11) * 4u, sm.fl[it % NB][0] + 64 * w);
   };
 
   // candidate stores go through a buffer resource over this wave's lists of the slice
@@ -778,7 +789,7 @@ __global__ __launch_bounds__(256, 2) void extra_tile_kernel(Problem P) {
         }
       }
     };
-    for (int it = 0; it < XNB - 1 && it < ntile; ++it) issue(it);
+    for (int it = 0; it < NB - 1 && it < ntile; ++it) issue(it);
     // the previous tile's scores, stored one tile late
     f32x16_t pc0 = {}, pc1 = {};
     bool pon = false;
@@ -786,19 +797,19 @@ __global__ __launch_bounds__(256, 2) void extra_tile_kernel(Problem P) {
 #pragma unroll 1
     for (int it = 0; it < ntile; ++it) {
       const int t0 = t_lo + it * XTOK, j = t0 >> 6;
-      wait_tiles<OPS>(min(XNB - 2, ntile - 1 - it));
+      wait_tiles<OPS>(min(NB - 2, ntile - 1 - it));
       tile_barrier();
-      const bool cand = row_ok && j < P.M && !FlagCopy::kept(sm.fl[it % XNB][0], j);
+      const bool cand = row_ok && j < P.M && !FlagCopy::kept(sm.fl[it % NB][0], j);
       // every wave has read this tile's flags before its buffer is refilled (a tile later)
-      if (it + XNB - 1 < ntile) issue(it + XNB - 1);
+      if (it + NB - 1 < ntile) issue(it + NB - 1);
       append(pc0, pon, ptw);
       append(pc1, pon, ptw + 32);
       // the next tile appends at most 32 entries per lane
       full = full || (addr - my_off) > static_cast<uint32_t>(2 * (HALF - 2 * 16)) * 8u;
       pon = false;
       if (wave_on && __ballot(cand) != 0) {
-        pc0 = T.scores(sm.k[it % XNB], 0);
-        pc1 = T.scores(sm.k[it % XNB], 1);
+        pc0 = T.scores(sm.k[it % NB], 0);
+        pc1 = T.scores(sm.k[it % NB], 1);
         pon = cand && !full;
         ptw = t0;
       }
@@ -880,7 +891,7 @@ __global__ __launch_bounds__(256, 2) void extra_tile_kernel(Problem P) {
       return bits;
     };
 
-    for (int it = 0; it < XNB - 1 && it < ntile; ++it) issue(it);
+    for (int it = 0; it < NB - 1 && it < ntile; ++it) issue(it);
     // the previous tile's scores and candidate bits, stored one tile late
     f32x16_t pc0 = {}, pc1 = {};
     uint32_t pb0 = 0, pb1 = 0;
@@ -888,17 +899,17 @@ __global__ __launch_bounds__(256, 2) void extra_tile_kernel(Problem P) {
 #pragma unroll 1
     for (int it = 0; it < ntile; ++it) {
       const int t0 = t_lo + it * XTOK, j = t0 >> 6;
-      wait_tiles<OPS>(min(XNB - 2, ntile - 1 - it));
+      wait_tiles<OPS>(min(NB - 2, ntile - 1 - it));
       tile_barrier();
-      const bool cand = row_ok && j < P.M && !FlagCopy::kept(sm.fl[it % XNB][0], j);
+      const bool cand = row_ok && j < P.M && !FlagCopy::kept(sm.fl[it % NB][0], j);
       // every wave has read this tile's flags before its buffer is refilled (a tile later)
-      if (it + XNB - 1 < ntile) issue(it + XNB - 1);
+      if (it + NB - 1 < ntile) issue(it + NB - 1);
       append(pc0, pb0, ptw);
       append(pc1, pb1, ptw + 32);
       pb0 = pb1 = 0;
       if (wave_on && __ballot(cand) != 0) {
-        pc0 = T.scores(sm.k[it % XNB], 0);
-        pc1 = T.scores(sm.k[it % XNB], 1);
+        pc0 = T.scores(sm.k[it % NB], 0);
+        pc1 = T.scores(sm.k[it % NB], 1);
         if (cand) {
           pb0 = cand_bits(pc0);
           pb1 = cand_bits(pc1);
