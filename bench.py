@@ -238,20 +238,32 @@ def kernel_rooflines(w, kern, sel, call_stats, qk_fp8, peaks):
     rate("block_score", 2.0 * BH * Mq * M * w.d, 1e12, "fp32", PEAK_FP32_TFLOPS, mb.get("fp32_mfma_TFLOPs"))
     sel_alg = BH * Mq * (M * 4 + 8 + Mpad // 8)
     rate("block_select", sel_alg, 1e9, "hbm", PEAK_HBM_GBS, mb.get("copy_GBs"), algorithmic_bytes=sel_alg)
-    rate("extra_select", 2.0 * 2.0 * BH * Mq * w.N * w.d, 1e12, "mfma", PEAK_BF16_TFLOPS, mb.get("bf16_mfma_TFLOPs"))
+    f32 = w.dtype == "fp32"
+    if f32:
+        # fp32: exact dot products on the vector unit (one product per candidate pair)
+        rate("extra_select", 2.0 * BH * Mq * w.N * w.d, 1e12, "fp32", PEAK_FP32_TFLOPS, None)
+    else:
+        rate("extra_select", 2.0 * 2.0 * BH * Mq * w.N * w.d, 1e12, "mfma", PEAK_BF16_TFLOPS,
+             mb.get("bf16_mfma_TFLOPs"))
     f_exact = 4.0 * w.d * call_stats["exact_pairs"]
     # the fp8-QK flavour runs half of the exact work (Q K^T) at the fp8 peak and half (P V) at
-    # the bf16 peak: its ceiling is the work-weighted harmonic mix of the two
-    peak = PEAK_BF16_TFLOPS if not qk_fp8 else 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
-    rate("sparse_flash_fwd", f_exact, 1e12, "mfma", peak, None if qk_fp8 else mb.get("bf16_mfma_TFLOPs"))
+    # the bf16 peak: its ceiling is the work-weighted harmonic mix of the two; fp32 tensors run
+    # both products on the fp32 matrix instruction
+    if f32:
+        peak, mpeak = PEAK_FP32_TFLOPS, mb.get("fp32_mfma_TFLOPs")
+    elif qk_fp8:
+        peak, mpeak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS), None
+    else:
+        peak, mpeak = PEAK_BF16_TFLOPS, mb.get("bf16_mfma_TFLOPs")
+    rate("sparse_flash_fwd", f_exact, 1e12, "mfma", peak, mpeak)
     t_flash = kern["sparse_flash_fwd"]["avg_ms"] * 1e-3
     ach = f_exact / t_flash / 1e12
     roof = dict(bound="mfma", achieved=round(ach, 2), peak=round(peak, 1), unit="TFLOP/s",
                 frac=round(ach / peak, 4), traffic=measured_traffic(w.name),
                 kernel="sparse_flash_fwd", algorithmic_flop=f_exact)
-    if peaks and not qk_fp8:
-        roof["measured_peak"] = peaks["bf16_mfma_TFLOPs"]
-        roof["frac_measured_peak"] = round(ach / peaks["bf16_mfma_TFLOPs"], 4)
+    if peaks and mpeak:
+        roof["measured_peak"] = mpeak
+        roof["frac_measured_peak"] = round(ach / mpeak, 4)
     return roof
 
 
@@ -427,7 +439,7 @@ def main():
         "cpu_baseline": cpu,
         "measured_peaks": peaks,
         "effective_tflops": round(f_exact / (ms_per_call * 1e-3) / 1e12, 2),
-        "mfma_util": round(f_exact / (ms_per_call * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "mfma_util": round(f_exact / (ms_per_call * 1e-3) / 1e12 / roof["peak"], 4),
         "kept_fraction": round(kept_frac, 4),
         "exact_tflop": round(f_exact / 1e12, 4),
         "centroid_tflop": round(f_cent / 1e12, 4),

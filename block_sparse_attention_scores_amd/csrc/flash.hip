@@ -18,7 +18,7 @@
 // max and sum are fp32 and kept per lane (the two half-waves hold the same query rows and
 // combine their partial sums at the end).  Logits are taken in base 2.
 //
-// fp32 kernel: one thread per query row, exact fp32 dot products, the same three phases.
+// fp32 tensors: flash_f32.hip (the same phases on the fp32 matrix instruction).
 #include "common.h"
 #include "launch.h"
 
@@ -647,127 +647,6 @@ __global__ __launch_bounds__(256, 2) void sparse_flash_fp8qk_kernel(Problem P) {
   sparse_flash_body<D, WPQ, G, true>(P);
 }
 
-// fp32 path: workgroup -> (head, query block), dense query blocks (the heaviest) first.
-__device__ __forceinline__ void flash_work(const Problem& P, int g, int* bh, int* qi) {
-  const int nd = P.dense_q1 - P.dense_q0;
-  const int BH = P.B * P.H;
-  if (g < BH * nd) {
-    *bh = g / nd;
-    *qi = P.dense_q0 + g % nd;
-    return;
-  }
-  g -= BH * nd;
-  const int ns = P.Mq - nd;
-  *bh = g / ns;
-  const int r = g % ns;
-  *qi = r < P.dense_q0 ? r : r + nd;
-}
-
-template <int D, int BQ>
-__global__ __launch_bounds__(BQ) void sparse_flash_f32_kernel(Problem P) {
-  // every thread reads the same key row at a time, so rows come straight from the cache
-  __shared__ const float* krow[64];
-  __shared__ const float* vrow[64];
-  __shared__ float bias[64];
-  int bh, qi;
-  flash_work(P, blockIdx.x, &bh, &qi);
-  const int tid = threadIdx.x;
-  const int b = bh / P.H, hh = bh % P.H;
-  const size_t row = (size_t)bh * P.Mq + qi;
-  const float* Kb = static_cast<const float*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)hh * P.k.sh;
-  const float* Vb = static_cast<const float*>(P.v.p) + (int64_t)b * P.v.sb + (int64_t)hh * P.v.sh;
-  const float* Qb = static_cast<const float*>(P.q.p) + (int64_t)b * P.q.sb + (int64_t)hh * P.q.sh;
-  const int qrow = (qi + P.q0) * BQ + tid;
-
-  float q[D], o[D];
-#pragma unroll
-  for (int e = 0; e < D; ++e) {
-    q[e] = Qb[(int64_t)qrow * P.q.sn + e];
-    o[e] = 0.f;
-  }
-  const bool dense = qi >= P.dense_q0 && qi < P.dense_q1;
-  const int nk = P.kept_cnt[row];
-  const int ne = dense ? 0 : P.extra_cnt[row];
-  const int nx = (ne + 63) / 64;
-  const int nc = (P.mode == 0 && !dense && nk < P.M) ? P.Mpad / 64 : 0;
-  const int ntiles = nk + nx + nc;
-  const int* klist = P.kept_idx + row * P.M;
-  const int* elist = P.extra_idx + row * MAX_EXTRA;
-  const uint8_t* mrow = P.mult + row * P.Mpad;
-  const float sl2 = P.scale * LOG2E;
-  float m_run = -__builtin_inff(), l_run = 0.f;
-
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    if (tid < 64) {
-      const int r = tid;
-      const float* kp = Kb;
-      const float* vp = Vb;
-      float bv = -__builtin_inff();
-      if (t < nk) {
-        const int tok = klist[t] * 64 + r;
-        kp = Kb + (int64_t)tok * P.k.sn;
-        vp = Vb + (int64_t)tok * P.v.sn;
-        bv = 0.f;
-      } else if (t < nk + nx) {
-        const int ei = (t - nk) * 64 + r;
-        if (ei < ne) {
-          const int tok = elist[ei];
-          kp = Kb + (int64_t)tok * P.k.sn;
-          vp = Vb + (int64_t)tok * P.v.sn;
-          bv = 0.f;
-        }
-      } else {
-        const int j = (t - nk - nx) * 64 + r;
-        const int m = mrow[j];            // 0 for kept blocks and for padding beyond M
-        if (m > 0) {
-          kp = P.kbar + ((size_t)bh * P.M + j) * D;
-          vp = P.vbar + ((size_t)bh * P.M + j) * D;
-          bv = __log2f(static_cast<float>(m));
-        }
-      }
-      krow[r] = kp;
-      vrow[r] = vp;
-      bias[r] = bv;
-    }
-    __syncthreads();
-    float sc[64];
-    float mx = -__builtin_inff();
-    for (int r = 0; r < 64; ++r) {
-      float x = -__builtin_inff();
-      if (bias[r] != -__builtin_inff()) {
-        const float* kp = krow[r];
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < D; ++e) s = fmaf(q[e], kp[e], s);
-        x = s * sl2 + bias[r];
-      }
-      sc[r] = x;
-      mx = fmaxf(mx, x);
-    }
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    l_run *= alpha;
-#pragma unroll
-    for (int e = 0; e < D; ++e) o[e] *= alpha;
-    for (int r = 0; r < 64; ++r) {
-      if (sc[r] == -__builtin_inff()) continue;
-      const float p = exp2f(sc[r] - m_use);
-      l_run += p;
-      const float* vp = vrow[r];
-#pragma unroll
-      for (int e = 0; e < D; ++e) o[e] = fmaf(p, vp[e], o[e]);
-    }
-    m_run = m_new;
-  }
-  float* Ob = static_cast<float*>(const_cast<void*>(P.o.p)) + (int64_t)b * P.o.sb +
-              (int64_t)hh * P.o.sh + (int64_t)qrow * P.o.sn;
-  const float inv = 1.f / l_run;
-#pragma unroll
-  for (int e = 0; e < D; ++e) Ob[e] = o[e] * inv;
-}
-
 hipError_t launch_sparse_flash(const Problem& P, hipStream_t stream) {
   if (P.dtype == 0) {
     const int G = P.bq == 64 ? 2 : 1;
@@ -790,14 +669,7 @@ hipError_t launch_sparse_flash(const Problem& P, hipStream_t stream) {
       else hipLaunchKernelGGL((sparse_flash_bf16_kernel<64, 4, 1>), grid, dim3(256), 0, stream, P);
     }
   } else {
-    dim3 grid(P.B * P.H * P.Mq);
-    if (P.bq == 64) {
-      if (P.d == 128) hipLaunchKernelGGL((sparse_flash_f32_kernel<128, 64>), grid, dim3(64), 0, stream, P);
-      else hipLaunchKernelGGL((sparse_flash_f32_kernel<64, 64>), grid, dim3(64), 0, stream, P);
-    } else {
-      if (P.d == 128) hipLaunchKernelGGL((sparse_flash_f32_kernel<128, 128>), grid, dim3(128), 0, stream, P);
-      else hipLaunchKernelGGL((sparse_flash_f32_kernel<64, 128>), grid, dim3(128), 0, stream, P);
-    }
+    return launch_sparse_flash_f32(P, stream);
   }
   return hipGetLastError();
 }

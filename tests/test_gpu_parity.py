@@ -151,6 +151,18 @@ def test_pairing_stride_on_a_96_wide_grid():
         assert int(np.argmin(tot)) + 1 == 3, tot
 
 
+@pytest.mark.parametrize("mode,bq", [("sol", 64), ("sla", 128)])
+def test_fp32_d128_both_block_sizes(mode, bq):
+    # the fp32 attention kernel at d = 128 with 64- and 128-row query blocks (two tile slots
+    # merged at the end, or four waves on one slot), extra tokens and dense rows, every output
+    # row against the oracle
+    x = random_qkv(1, 2, 4096, 128, seed=13, dtype="fp32")
+    w = workload(1, d=128, mode=mode, block_q=bq, keep_percent=20.0, extra_tokens=96, sink_range=64,
+                 dense_rows=(3584, 4096))
+    x.w = w
+    run_and_check(w, x, range(2))
+
+
 @pytest.mark.parametrize("extra", [0, 64])
 def test_local3d_fp32_tiny(extra):
     # 32-token rows: a block holds two rows, so the pattern is a line of blocks plus frame hops
