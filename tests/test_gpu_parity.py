@@ -419,6 +419,30 @@ def test_finite_check_counts_nonfinite_values(dtype):
     assert stats[7].item() == 3 + n_out
 
 
+def test_finite_check_counts_only_the_window_rows():
+    # a query-row window leaves the other rows of out untouched; filled with NaN there, they
+    # must not be counted: the count is the non-finite inputs plus the window's outputs
+    x = random_qkv(1, 2, 2048, 64, seed=9, dtype="bf16")
+    q, k, v = device_inputs(x)
+    out = torch.full_like(q, float("nan"))
+    stats = torch.zeros(sa.NSTATS, dtype=torch.int64, device="cuda")
+    print("\n[finite] window rows 512..1024, clean inputs", flush=True)
+    sa.sol_attn(q, k, v, tau=1.3, out=out, q_rows=(512, 1024), stats=stats, flags=sa.FLAG_CHECK_FINITE)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[:, :, 512:1024].float()).all()
+    assert torch.isnan(out[:, :, :512].float()).all() and torch.isnan(out[:, :, 1024:].float()).all()
+    assert stats[7].item() == 0
+    k[0, 0, 3, 1] = float("nan")            # a sink-range key: every row of head 0 attends it
+    stats.zero_()
+    print("[finite] window rows 512..1024, one NaN key", flush=True)
+    sa.sol_attn(q, k, v, tau=1.3, sink_range=64, out=out, q_rows=(512, 1024), stats=stats,
+                flags=sa.FLAG_CHECK_FINITE)
+    torch.cuda.synchronize()
+    n_win = int((~torch.isfinite(out[:, :, 512:1024].float())).sum().item())
+    assert n_win > 0
+    assert stats[7].item() == 1 + n_win
+
+
 @pytest.mark.parametrize("mode", ["sol", "sla", "local3d"])
 def test_fp8qk_flavour(mode):
     # the fp8-QK flavour: the selection must be the bf16 path's, bit for bit, and the output
