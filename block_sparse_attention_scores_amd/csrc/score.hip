@@ -25,8 +25,10 @@ __global__ __launch_bounds__(256) void block_score_kernel(Problem P) {
   const int tid = threadIdx.x, l = tid % 64, w = tid / 64;
   const int c32 = l % 32, h = l / 32;
   const int wi = 64 * (w / 2), wj = 64 * (w % 2);   // this wave's 64x64 sub-tile
-  const float* qb = P.qbar + (size_t)bh * P.Mq * D;
-  const float* kb = P.kbar + (size_t)bh * P.M * D;
+  // buffer resources over this head's pooled rows: rows past Mq (M) read zero, so the loads
+  // need no branch; a slice's loads are issued while the previous slice is multiplied
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(P.qbar + (size_t)bh * P.Mq * D, static_cast<uint32_t>(P.Mq) * D * 4u);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(P.kbar + (size_t)bh * P.M * D, static_cast<uint32_t>(P.M) * D * 4u);
 
   f32x16_s acc[2][2];
 #pragma unroll
@@ -34,21 +36,32 @@ __global__ __launch_bounds__(256) void block_score_kernel(Problem P) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16_s{};
 
-  for (int d0 = 0; d0 < D; d0 += DC) {
-    __syncthreads();
-    // 128 rows x 32 floats of each operand: 1024 float4 per operand, four per thread
+  // 128 rows x 32 floats of each operand per slice: 1024 float4 per operand, four per thread
+  typedef float f32x4_s __attribute__((ext_vector_type(4)));
+  f32x4_s xq[4], yk[4];
+  auto fetch = [&](int d0) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int idx = tid + 256 * u, r = idx / 8, c4 = idx % 8;
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
-      if (i0 + r < P.Mq) x = *reinterpret_cast<const float4*>(qb + (size_t)(i0 + r) * D + d0 + 4 * c4);
-      if (j0 + r < P.M) y = *reinterpret_cast<const float4*>(kb + (size_t)(j0 + r) * D + d0 + 4 * c4);
+      xq[u] = __builtin_bit_cast(f32x4_s, __builtin_amdgcn_raw_buffer_load_b128(
+                  qrs, static_cast<uint32_t>(((i0 + r) * D + d0 + 4 * c4) * 4), 0, 0));
+      yk[u] = __builtin_bit_cast(f32x4_s, __builtin_amdgcn_raw_buffer_load_b128(
+                  krs, static_cast<uint32_t>(((j0 + r) * D + d0 + 4 * c4) * 4), 0, 0));
+    }
+  };
+  fetch(0);
+  for (int d0 = 0; d0 < D; d0 += DC) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + 256 * u, r = idx / 8, c4 = idx % 8;
       float* a = As + r * LD + 4 * c4;
       float* b = Bs + r * LD + 4 * c4;
-      a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
-      b[0] = y.x; b[1] = y.y; b[2] = y.z; b[3] = y.w;
+      a[0] = xq[u].x; a[1] = xq[u].y; a[2] = xq[u].z; a[3] = xq[u].w;
+      b[0] = yk[u].x; b[1] = yk[u].y; b[2] = yk[u].z; b[3] = yk[u].w;
     }
     __syncthreads();
+    if (d0 + DC < D) fetch(d0 + DC);
     // step kk: lanes 0-31 supply dimension 2kk, lanes 32-63 dimension 2kk+1 (A row / B column c32)
 #pragma unroll 4
     for (int kk = 0; kk < DC / 2; ++kk) {

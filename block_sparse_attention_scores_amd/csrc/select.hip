@@ -344,9 +344,13 @@ __global__ __launch_bounds__(256) void block_select_reg_kernel(Problem P) {
   if (r >= (long)P.B * P.H * P.Mq) return;
   const int nu = (P.M + 63) >> 6;
   const float* s = P.scores + r * P.Mpad;
+  // buffer loads bounded by the row's M scores: columns past M read zero, so the loads need
+  // no branch and are all in flight together
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, static_cast<uint32_t>(P.M) * 4u);
   float v[RU];
 #pragma unroll
-  for (int u = 0; u < RU; ++u) v[u] = u < nu ? s[64 * u + lane] : 0.f;
+  for (int u = 0; u < RU; ++u)
+    v[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(64 * u + lane) * 4u, 0, 0));
   select_row<RU, MODE>(P, static_cast<int>(r / P.Mq), static_cast<int>(r % P.Mq), v, hist_all[wv], nullptr);
 }
 
@@ -364,15 +368,13 @@ __global__ __launch_bounds__(256) void block_select_sol_kernel(Problem P) {
   if (r >= (long)P.B * P.H * P.Mq) return;
   const int nu = (P.M + 63) >> 6;
   const float* s = P.scores + r * P.Mpad;
+  // buffer loads bounded by the row's M scores: the padding columns past M read zero, and the
+  // loads need no branch, so all of them are in flight together
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, static_cast<uint32_t>(P.M) * 4u);
   float v[RU];
 #pragma unroll
-  for (int u = 0; u < RU; ++u) {
-    v[u] = 0.f;
-    if (u < nu) {
-      const float x = s[64 * u + lane];
-      v[u] = 64 * u + lane < P.M ? x : 0.f;
-    }
-  }
+  for (int u = 0; u < RU; ++u)
+    v[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<uint32_t>(64 * u + lane) * 4u, 0, 0));
   select_row_sol<RU, LISTS>(P, static_cast<int>(r / P.Mq), static_cast<int>(r % P.Mq), v, wbuf_all[wv]);
 }
 
