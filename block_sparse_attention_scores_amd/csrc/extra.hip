@@ -41,6 +41,9 @@ constexpr int XSTEP = 32;   // tokens per wave step
 // Fill of a candidate list of the 16-bit sampled pass one of whose halves could have
 // overflowed (its query block goes to the exact pass).
 constexpr int EXTRA_PART_OVERFLOW = -1;
+// A half list that could overflow holds at least EXTRA_CAP / 2 - 32 candidates at or above the
+// seed, which must be at least E for the exact pass to start from the seed.
+static_assert(EXTRA_CAP / 2 - 32 >= MAX_EXTRA, "an overflowing half list holds E candidates");
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -700,9 +703,10 @@ __device__ __forceinline__ float key_threshold(uint32_t thr) {
 // lane l+32 to slots 2k+1, and at the end the longer lane closes the gaps after the shorter
 // one's last entry.  A lane that could overflow its half of the list stops appending and the
 // list's fill is marked EXTRA_PART_OVERFLOW, which sends the query block to the exact pass.
-// REPAIR = true: only the query blocks the merge flagged, from the lowest threshold (every
-// candidate competes: the exact selection), one list per (query block, slice) cut back to its
-// best E whenever the next step could overflow it.
+// REPAIR = true: only the query blocks the merge flagged, from the threshold the merge left
+// (the lowest after a short list, so every candidate competes: the exact selection; the seed
+// after an overflow), one list per (query block, slice) cut back to its best E whenever the
+// next step could overflow it.
 template <int D, bool REPAIR>
 __global__ __launch_bounds__(256, REPAIR ? 2 : 3) void extra_tile_kernel(Problem P) {
   constexpr bool repair = REPAIR;
@@ -732,7 +736,9 @@ __global__ __launch_bounds__(256, REPAIR ? 2 : 3) void extra_tile_kernel(Problem
   const int ntile = (t_hi - t_lo + XTOK - 1) / XTOK;           // N is a whole number of tiles
   TT T;
   T.init(P, row, i < P.Mq);
-  uint32_t thr = (!repair && row_ok) ? P.extra_seed[row] : 0u;
+  // the sampled pass starts from the seed; the exact pass from the threshold the merge left in
+  // extra_seed (zero, or the seed after an overflow)
+  uint32_t thr = row_ok ? P.extra_seed[row] : 0u;
   float tf = key_threshold(thr);
   const bool wave_on = __ballot(row_ok) != 0;
 
@@ -986,7 +992,10 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) 
   const int* part = P.extra_part + row * nl;
   const uint2* lists = P.extra_buf + row * nl * EXTRA_CAP;
   if (repair == 2) {                                       // exact selection for every row
-    if (l == 0) P.extra_flag[row] = 1;
+    if (l == 0) {
+      P.extra_flag[row] = 1;
+      P.extra_seed[row] = 0u;                              // from the lowest threshold
+    }
     return;
   }
   if (repair && P.extra_flag[row] == 0) return;
@@ -1003,11 +1012,19 @@ __global__ __launch_bounds__(64) void extra_merge_kernel(Problem P, int repair) 
   if (!repair) {
     // every candidate scoring at or above the seeded threshold is in the lists; fewer than
     // min(E, |candidates|) of them means the seed was too high, and a list that could have
-    // overflowed may have lost some: either way the query block goes to the exact repair pass
+    // overflowed may have lost some: either way the query block goes to the exact repair pass.
+    // That pass starts from the threshold left in extra_seed: zero after a short list (every
+    // candidate competes); the seed itself after an overflow, since a half list holding more
+    // than EXTRA_CAP / 2 - 32 >= E candidates at or above the seed means no candidate below it
+    // can be among the E best.
     const int ncand = P.N - P.bk * P.kept_cnt[row];
-    const bool short_ = overflow || total < min(E, ncand);
-    if (l == 0) P.extra_flag[row] = short_ ? 1 : 0;
-    if (short_) return;
+    const bool short_ = total < min(E, ncand);
+    const bool flag = overflow || short_;
+    if (l == 0) {
+      P.extra_flag[row] = flag ? 1 : 0;
+      if (flag && !overflow) P.extra_seed[row] = 0u;
+    }
+    if (flag) return;
   }
   // the lists as one flat range: entry p lives in list q with start[q] <= p < start[q+1]
   int start[17];
