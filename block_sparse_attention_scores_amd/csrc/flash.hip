@@ -346,6 +346,32 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
     }
     if (w == 0) sm.bias[bf][gg][l] = e0 + l < cnt ? 0.f : -__builtin_inff();
   };
+  // ---- step j of the pair's extra tokens into buffer bf: rows 0-31 are block 0's tokens
+  // 32j .. 32j+31, rows 32-63 block 1's (rows past a block's count repeat one of its tokens, or
+  // the other block's when it has none, and get bias -inf), so each half of the workgroup works
+  // on its own block's half of the tile
+  const int ne0 = ne[0], ne1 = ne[1];
+  auto issue_extra_pair = [&](int j, int bf) {
+    char* kd = reinterpret_cast<char*>(sm.k[bf]) + w * 1024;
+    char* vd = reinterpret_cast<char*>(sm.v[bf]) + w * 1024;
+    const uint32_t vcol0 = ((static_cast<uint32_t>(l) % KCH) ^ (krow0 & 4)) << 4;
+#pragma unroll
+    for (int u = 0; u < PER_THREAD; ++u) {
+      const int r = krow0 + KSTEP * u;
+      const bool second = r >= 32;
+      const int cnt = second ? ne1 : ne0;
+      const int e = 32 * j + (r & 31);
+      const int* el = (second == (cnt > 0)) ? sm.eidx[1] : sm.eidx[0];
+      const size_t tok = static_cast<uint32_t>(el[e < cnt ? e : 0]);
+      glb_to_lds16(reinterpret_cast<const char*>(Kb) + tok * ksn_b + kcol0, kd + u * 4096);
+      glb_to_lds16(reinterpret_cast<const char*>(Vb) + tok * vsn_b + vcol0, vd + u * 4096);
+    }
+    if (w == 0) {
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+        sm.bias[bf][gg][l] = ((l >> 5) == gg && 32 * j + (l & 31) < (gg ? ne1 : ne0)) ? 0.f : -__builtin_inff();
+    }
+  };
 
   f32x16_t o[D / 32];
 #pragma unroll
@@ -521,6 +547,56 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
     }
   };
 
+  // ---- one 32-key half h of a gathered tile (row-major V): the score products of K rows
+  // 32h..32h+31, the online-softmax step and the value products of the half's two 16-key steps
+  auto compute_half_rm = [&](int bf, int h, f32x16_t& sh) {
+    const char* kt_ = reinterpret_cast<const char*>(sm.k[bf]) + h * 32 * D * 2;
+    const char* vt_ = reinterpret_cast<const char*>(sm.v[bf]);
+    __builtin_amdgcn_s_setprio(1);
+    {
+      bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt_ + ak);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        bf16x8_t n = a;
+        if (ks + 1 < D / 16) n = *reinterpret_cast<const bf16x8_t*>(kt_ + (ak ^ (32u * (ks + 1))));
+        sh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sh, 0, 0, 0);
+        a = n;
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    rescale(half_max(sh));
+    const float nm = m_run == -__builtin_inff() ? 0.f : -m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      bf16x8_t pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pf[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sh[8 * st + e], sl2, nm)));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2_t pp = {pf[2 * e], pf[2 * e + 1]};
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
+      }
+      // one fragment of the row-major V tile at a time: element e = V[16ks + 8(e/4) + 4h32 +
+      // e%4][32dt + c32], ks = 2h + st
+      const int ks = 2 * h + st;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const char* base = vt_ + (rmo + ((64u * dt) ^ rmx)) + ks * 32 * D;
+        uint32_t x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          x[e] = *reinterpret_cast<const uint16_t*>(base + (8 * (e >> 2) + (e & 3)) * 2 * D);
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t pk = {x[0] | (x[1] << 16), x[2] | (x[3] << 16), x[4] | (x[5] << 16), x[6] | (x[7] << 16)};
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, pk), pf, o[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    l_run += psum;
+  };
+
   if (tid < 64) sm.zero[tid] = 0.f;       // visible after the first barrier of the loop
   // the pair's extra-token lists go to LDS now (wave g copies block g's, 16 bytes a lane) and
   // arrive with the first tile, so the gather after the main loop reads its indices from LDS
@@ -543,9 +619,37 @@ __device__ __forceinline__ void sparse_flash_body(const Problem& P) {
     bf ^= 1;
   }
 
-  // ---- bf16: the extra tokens, up to 4 tiles of 64 per query block (block 0's, then block
-  // 1's), gathered straight to LDS and double-buffered like the main loop's tiles
-  if constexpr (!QK8) {
+  // ---- bf16: the extra tokens, gathered straight to LDS and double-buffered like the main
+  // loop's tiles; pairs of 64-row blocks take 32 tokens of each block per step (every wave
+  // busy), single 128-row blocks up to 4 tiles of 64
+  if constexpr (!QK8 && G == 2) {
+    // step i: 32 tokens of each block of the pair, each half of the workgroup on its own block
+    const int nstep = (max(ne0, ne1) + 31) / 32;
+    const int neg = g ? ne1 : ne0;
+    if (nstep > 0) {
+      __syncthreads();                    // every wave is done with the main loop's buffers
+      issue_extra_pair(0, 0);
+#pragma unroll 1
+      for (int i = 0; i < nstep; ++i) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (i + 1 < nstep) issue_extra_pair(i + 1, (i + 1) & 1);
+        if (wave_on && 32 * i < neg) {
+          f32x16_t sh;
+          const float* bias = sm.bias[i & 1][g] + 32 * g;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const float4 bv = *reinterpret_cast<const float4*>(bias + r4 * 8 + 4 * h32);
+            sh[4 * r4 + 0] = bv.x;
+            sh[4 * r4 + 1] = bv.y;
+            sh[4 * r4 + 2] = bv.z;
+            sh[4 * r4 + 3] = bv.w;
+          }
+          compute_half_rm(i & 1, g, sh);
+        }
+      }
+    }
+  } else if constexpr (!QK8) {
     // tile j: block 0's tiles 0 .. nx0-1, then block 1's
     const int nx0 = (ne[0] + 63) / 64, nx = nx0 + (ne[1] + 63) / 64;
     auto issue_tile = [&](int j) { issue_extra(j < nx0 ? 0 : 1, 64 * (j < nx0 ? j : j - nx0), j & 1); };
