@@ -114,9 +114,12 @@ def cpu_baseline(w, x, heads=(0,), n_sparse=24, n_dense=4, seed=7):
     from oracle import solattn
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] + [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info})) or "unknown"
     except Exception:  # pragma: no cover
-        cores = 1
+        cores, blas = 1, "unknown"
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     p = dict(block_q=w.block_q, block_k=w.block_k, tau=w.tau, keep_percent=w.keep_percent,
              sink_range=w.sink_range, extra_tokens=w.extra_tokens, dense_rows=w.dense_rows)
     if w.mode == "local3d":
@@ -157,7 +160,8 @@ def cpu_baseline(w, x, heads=(0,), n_sparse=24, n_dense=4, seed=7):
               f"{len(t_sparse)} sparse + {len(t_dense)} dense query blocks attended "
               f"({per_sparse * 1e3:.1f} / {per_dense * 1e3:.1f} ms each); extrapolated to "
               f"{BH} heads x {Mq} query blocks")
-    return dict(value=total * 1e3, unit="ms", cores=int(cores), kind="oracle", sample=sample), refs
+    return dict(value=total * 1e3, unit="ms", cores=int(cores), kind="oracle", sample=sample,
+                blas=blas, host_cpus=int(affinity)), refs
 
 
 def selection_check(w, sel, refs):
@@ -189,7 +193,8 @@ def selection_check(w, sel, refs):
 
 def measured_peaks(torch, sa, dev):
     """What the matrix cores and HBM deliver here: a bf16 and an fp32 matrix-instruction loop
-    and a 1 GiB device copy (solattn_peak_probe), best of five launches each."""
+    and a 1 GiB device copy (solattn_peak_probe), best of five launches each, and the shader
+    clock observed during the bf16 loop (median of three launches)."""
     buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
     out = {}
     for kind, iters, name, scale in ((0, 400, "bf16_mfma_TFLOPs", 1e12), (1, 40, "fp32_mfma_TFLOPs", 1e12),
@@ -204,6 +209,16 @@ def measured_peaks(torch, sa, dev):
             if rep:                                 # the first launch warms up
                 best = max(best, work / (e0.elapsed_time(e1) * 1e-3) / scale)
         out[name] = round(best, 1)
+    # the shader clock while every matrix core is busy: clock and wall-clock ticks of one wave
+    clocks = []
+    for rep in range(3):
+        rate = sa.peak_probe(3, buf, 400)
+        torch.cuda.synchronize()
+        ticks = buf[:16].view(torch.int64).cpu().tolist()
+        if ticks[1] > 0:
+            clocks.append(ticks[0] / (ticks[1] / rate) / 1e9)
+    if clocks:
+        out["clock_GHz_under_mfma_load"] = round(sorted(clocks)[len(clocks) // 2], 3)
     del buf
     torch.cuda.empty_cache()
     return out

@@ -442,6 +442,15 @@ struct ExtraSampledSmem {
   int any;
 };
 
+// The seeds' pass: three tile buffers as well; a tile's two sampled runs share one flag array
+// (lane l < 32 of wave w holds its query block's bitmap dword of run 0's key block at 64w + l,
+// lane l + 32 that of run 1's block at 64w + 32 + l), so three workgroups fit a compute unit.
+template <int D>
+struct ExtraSeedSmem {
+  uint16_t k[XNB_S][XTOK * D];
+  uint32_t fl[XNB_S][256];
+};
+
 // Barrier for the tile loop: every wave has waited for its own copies of the tile (vmcnt), so
 // after it the whole tile is in LDS; the memory clobber keeps LDS accesses on their side.  No
 // memory fence: a fence would wait for every outstanding copy, including the later tiles'.
@@ -483,6 +492,17 @@ struct FlagCopy {
   }
   __device__ static bool kept(const uint32_t* src, int j) {
     return (src[threadIdx.x] >> (j & 31)) & 1u;
+  }
+  // both runs of a tile in one copy: lanes 0-31 take key block j0's dword, lanes 32-63 j1's
+  __device__ void issue_pair(int j0, int j1, uint32_t* dst) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int j = (threadIdx.x & 63) < 32 ? j0 : j1;
+    buf_to_lds4(rs, row_off + static_cast<uint32_t>(j >> 5) * 4u, dst + 64 * w);
+  }
+  // run q's flag of this lane's query block from an issue_pair copy
+  __device__ static bool kept_pair(const uint32_t* src, int q, int j) {
+    const int t = threadIdx.x;
+    return (src[(t & ~63) + 32 * q + (t & 31)] >> (j & 31)) & 1u;
   }
 };
 
@@ -585,8 +605,9 @@ __host__ __device__ inline int xcd_grid(int units, int ngrp) { return (units + 7
 // chosen so that about SAMPLE_MARGIN * E candidates are expected at or above it.  A best-of-a-
 // subset is at most the best of the whole sample, so the seed only errs low (more candidates).
 template <int D>
-__global__ __launch_bounds__(256, 2) void extra_seed_kernel(Problem P) {
-  __shared__ ExtraSmem<D> sm;
+__global__ __launch_bounds__(256, 3) void extra_seed_kernel(Problem P) {
+  __shared__ ExtraSeedSmem<D> sm;
+  constexpr int NB = XNB_S;
   using TT = ExtraTiles<D>;
   int bh, grp;
   if (!xcd_unit(P.B * P.H, (P.Mq + EXTRA_GROUP_BF16 - 1) / EXTRA_GROUP_BF16, &bh, &grp)) return;
@@ -606,13 +627,12 @@ __global__ __launch_bounds__(256, 2) void extra_seed_kernel(Problem P) {
   const int nsteps = min(2 * P.M, min(4 * SAMPLE_STEPS, max(SAMPLE_STEPS, P.N / 1024)));
   const int ntile = (nsteps + 1) / 2;
   auto run_tok = [&](int s) { return sample_run(s < nsteps ? s : 0, nsteps, P.M); };
-  constexpr int OPS = TT::PT + 2;          // copies per thread per tile: keys, two flag dwords
+  constexpr int OPS = TT::PT + 1;          // copies per thread per tile: keys, one flag dword
   auto issue = [&](int it) {
-    T.issue(sm.k[it % XNB], [&](int q) {
+    T.issue(sm.k[it % NB], [&](int q) {
       return std::make_pair(kbase + (int64_t)run_tok(2 * it + q) * P.k.sn, 32u * T.ksn_b);
     });
-#pragma unroll
-    for (int q = 0; q < 2; ++q) F.issue(run_tok(2 * it + q) >> 6, sm.fl[it % XNB][q]);
+    F.issue_pair(run_tok(2 * it) >> 6, run_tok(2 * it + 1) >> 6, sm.fl[it % NB]);
   };
   uint32_t best[4][SAMPLE_KEEP];
 #pragma unroll
@@ -620,36 +640,35 @@ __global__ __launch_bounds__(256, 2) void extra_seed_kernel(Problem P) {
 #pragma unroll
     for (int e = 0; e < SAMPLE_KEEP; ++e) best[q][e] = 0u;
   int nsamp = 0;
-  for (int it = 0; it < XNB - 1 && it < ntile; ++it) issue(it);
+  for (int it = 0; it < NB - 1 && it < ntile; ++it) issue(it);
 #pragma unroll 1
   for (int it = 0; it < ntile; ++it) {
-    wait_tiles<OPS>(min(XNB - 2, ntile - 1 - it));
+    wait_tiles<OPS>(min(NB - 2, ntile - 1 - it));
     tile_barrier();
     bool fl[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int s = 2 * it + q;
-      fl[q] = row_ok && s < nsteps && !FlagCopy::kept(sm.fl[it % XNB][q], run_tok(s) >> 6);
+      fl[q] = row_ok && s < nsteps && !FlagCopy::kept_pair(sm.fl[it % NB], q, run_tok(s) >> 6);
     }
-    // every wave has read this tile's flags before the tile's buffer is refilled (a tile later)
-    if (it + XNB - 1 < ntile) issue(it + XNB - 1);
+    // the refill goes to the buffer every wave finished with before this tile's barrier
+    if (it + NB - 1 < ntile) issue(it + NB - 1);
     if (wave_on) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const f32x16_t c = T.scores(sm.k[it % XNB], q);
+        const f32x16_t c = T.scores(sm.k[it % NB], q);
         if (fl[q]) {
           nsamp += 16;
           // run 2 it + q goes to list (2 it + q) % 4
+          // insertion into a list kept in descending order: entry e of the new list is the
+          // median of old entries e-1 and e and the new key (one median-of-three per entry)
           auto put = [&](uint32_t* bl) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              uint32_t k = float_key(c[r]);
+              const uint32_t k = float_key(c[r]);
 #pragma unroll
-              for (int e = 0; e < SAMPLE_KEEP; ++e) {
-                const uint32_t hi = max(bl[e], k), lo = min(bl[e], k);
-                bl[e] = hi;
-                k = lo;
-              }
+              for (int e = SAMPLE_KEEP - 1; e > 0; --e) bl[e] = med3_u32(bl[e - 1], bl[e], k);
+              bl[0] = max(bl[0], k);
             }
           };
           if (it & 1) put(best[2 + q]);

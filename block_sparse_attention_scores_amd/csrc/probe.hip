@@ -5,6 +5,9 @@
 //   kind 1: fp32 32x32x2 matrix instructions, likewise
 //   kind 2: device copy of bytes/2 bytes from the first half of buf to the second (16-byte
 //           vector loads and stores, grid-stride), the HBM streaming rate
+//   kind 3: the kind-0 loop with the first wave of workgroup 0 reading the shader clock counter
+//           and the constant-rate wall clock counter before and after it: their ratio times
+//           the wall clock's rate is the shader clock while every matrix core is busy
 // The caller times the launch on its stream (events) and divides the work (flop_per_launch or
 // the bytes moved) by the time.
 #include "../../include/solattn.h"
@@ -37,6 +40,35 @@ __global__ __launch_bounds__(PROBE_THREADS) void mfma_bf16_probe(float* out, int
 #pragma unroll
   for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
   if (s == 1.2345f) out[blockIdx.x * PROBE_THREADS + threadIdx.x] = s;   // keeps the loop live
+}
+
+// kind 3: out[0] = shader clock ticks, out[1] = wall clock ticks over the loop of wave 0 of
+// workgroup 0 (a vector store by its first lane)
+__global__ __launch_bounds__(PROBE_THREADS) void clock_probe(unsigned long long* out, int iters) {
+  const int l = threadIdx.x & 63;
+  bf16x8_p a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = static_cast<__bf16>(static_cast<float>((l + e) & 7) * 0.125f);
+    b[e] = static_cast<__bf16>(static_cast<float>((l * 3 + e) & 7) * 0.0625f);
+  }
+  f32x16_p c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  const unsigned long long t0 = clock64(), w0 = wall_clock64();
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  const unsigned long long t1 = clock64(), w1 = wall_clock64();
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    out[0] = t1 - t0;
+    out[1] = w1 - w0;
+  }
+  if (s == 1.2345f) reinterpret_cast<float*>(out)[4 + blockIdx.x * PROBE_THREADS + threadIdx.x] = s;
 }
 
 __global__ __launch_bounds__(PROBE_THREADS) void mfma_f32_probe(float* out, int iters) {
@@ -77,6 +109,15 @@ extern "C" int solattn_peak_probe(int kind, void* buf, size_t bytes, int iters, 
       hipLaunchKernelGGL(mfma_f32_probe, dim3(PROBE_WG), dim3(PROBE_THREADS), 0, s, static_cast<float*>(buf), iters);
       *work_per_launch = waves * iters * 4.0 * (2.0 * 32 * 32 * 2);
     }
+  } else if (kind == 3) {
+    if (bytes < (size_t)(PROBE_WG * PROBE_THREADS + 4) * sizeof(float)) return SOLATTN_EINVAL;
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+      return SOLATTN_EHIP;
+    hipLaunchKernelGGL(clock_probe, dim3(PROBE_WG), dim3(PROBE_THREADS), 0, s,
+                       static_cast<unsigned long long*>(buf), iters);
+    *work_per_launch = 1e3 * khz;              // the wall clock's rate in Hz
   } else if (kind == 2) {
     const size_t half = bytes / 2 / 16 * 16;
     if (half == 0) return SOLATTN_EINVAL;

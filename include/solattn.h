@@ -387,8 +387,13 @@ const char* solattn_kernel_name(int index);
  *   kind 0: bf16 32x32x16 matrix instructions in a loop, no memory (work: flop)
  *   kind 1: fp32 32x32x2 matrix instructions in a loop (work: flop)
  *   kind 2: copy of the first half of buf to its second half (work: bytes read + written)
- * buf: device memory, 16-byte aligned, at least 2 MiB for kinds 0 and 1 (results that are
- * never stored unless a sum hits one exact value); iters: loop trips for kinds 0 and 1 (>= 1).
+ *   kind 3: the kind-0 loop, timed from inside by its first wave: writes two unsigned 64-bit
+ *           counts to the start of buf (shader clock ticks, then wall clock ticks, over that
+ *           wave's loop) and sets *work_per_launch to the wall clock's rate in Hz, so that
+ *           ticks[0] / (ticks[1] / rate) is the shader clock under full matrix load; read the
+ *           counts after the stream has finished the launch
+ * buf: device memory, 16-byte aligned, at least 2 MiB for kinds 0, 1 and 3 (results that are
+ * never stored unless a sum hits one exact value); iters: loop trips for kinds 0, 1 and 3 (>= 1).
  * Returns SOLATTN_OK, SOLATTN_EINVAL or SOLATTN_EHIP.
  */
 int solattn_peak_probe(int kind, void* buf, size_t bytes, int iters, void* stream, double* work_per_launch);
