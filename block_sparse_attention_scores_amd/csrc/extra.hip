@@ -45,6 +45,11 @@ constexpr int EXTRA_PART_OVERFLOW = -1;
 // seed, which must be at least E for the exact pass to start from the seed.
 static_assert(EXTRA_CAP / 2 - 32 >= MAX_EXTRA, "an overflowing half list holds E candidates");
 
+// Median of three unsigned values (one v_med3_u32).
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));
+}
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   __builtin_amdgcn_wave_barrier();
