@@ -279,3 +279,18 @@ def test_noalloc_validates_before_any_device_call():
     o = sa.make_opts(workspace=1 << 40, workspace_bytes=1 << 30)
     assert L.sol_attn_fwd_noalloc(QP, KP, VP, OP, 1, 2, 4096, 64, 1.3, 64, 64, 0, 0, ctypes.byref(o)) == sa.EINVAL
     assert "workspace" in sa.last_error()
+
+
+def test_peak_probe_validates_before_any_device_call():
+    # unknown kinds, small or misaligned buffers and zero trips are refused on the host
+    L = sa.lib()
+    work = ctypes.c_double()
+    big = 64 << 20
+    assert L.solattn_peak_probe(0, None, big, 1, None, ctypes.byref(work)) == sa.EINVAL
+    assert L.solattn_peak_probe(0, QP, big, 0, None, ctypes.byref(work)) == sa.EINVAL
+    assert L.solattn_peak_probe(0, QP + 8, big, 1, None, ctypes.byref(work)) == sa.EINVAL
+    assert L.solattn_peak_probe(4, QP, big, 1, None, ctypes.byref(work)) == sa.EINVAL
+    assert L.solattn_peak_probe(0, QP, 1 << 20, 1, None, ctypes.byref(work)) == sa.EINVAL
+    assert L.solattn_peak_probe(3, QP, 1 << 20, 1, None, ctypes.byref(work)) == sa.EINVAL
+    assert L.solattn_peak_probe(2, QP, 16, 1, None, ctypes.byref(work)) == sa.EINVAL
+    assert L.solattn_peak_probe(0, QP, big, 1, None, None) == sa.EINVAL
