@@ -604,86 +604,23 @@ __device__ __forceinline__ bool xcd_unit(int units, int ngrp, int* unit, int* gr
 }
 __host__ __device__ inline int xcd_grid(int units, int ngrp) { return (units + 7) / 8 * 8 * ngrp; }
 
-// Seeds: the sample runs (sample_run) scored for the group's 128 query blocks, two runs per
-// tile.  Each lane keeps the SAMPLE_KEEP best keys of every fourth run (four lists), so a query
-// block's two lanes hold 64 of its best sample keys; the seed is the r-th best of them, with r
-// chosen so that about SAMPLE_MARGIN * E candidates are expected at or above it.  A best-of-a-
-// subset is at most the best of the whole sample, so the seed only errs low (more candidates).
-template <int D>
-__global__ __launch_bounds__(256, 3) void extra_seed_kernel(Problem P) {
-  __shared__ ExtraSeedSmem<D> sm;
-  constexpr int NB = XNB_S;
-  using TT = ExtraTiles<D>;
-  int bh, grp;
-  if (!xcd_unit(P.B * P.H, (P.Mq + EXTRA_GROUP_BF16 - 1) / EXTRA_GROUP_BF16, &bh, &grp)) return;
-  const int tid = threadIdx.x, l = tid % 64;
-  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int rl = l % 32, i = grp * EXTRA_GROUP_BF16 + 32 * w + rl;
-  const int b = bh / P.H, h = bh % P.H;
-  const size_t row = (size_t)bh * P.Mq + (i < P.Mq ? i : 0);
-  const bool row_ok = i < P.Mq && !(i >= P.dense_q0 && i < P.dense_q1);
-  const uint16_t* kbase = static_cast<const uint16_t*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)h * P.k.sh;
-  TT T;
-  T.init(P, row, i < P.Mq);
-  FlagCopy F;
-  F.init(P, bh, i);
-  const bool wave_on = __ballot(row_ok) != 0;
+// Workgroups of the seeds' pass per (head, group of 128 query blocks): with few groups the
+// sampled tiles are dealt round-robin to up to four workgroups, about three per compute unit
+// in all, so that more waves share each SIMD.
+__host__ __device__ inline int seed_splits(int B, int H, int Mq) {
+  const long groups = (long)((Mq + EXTRA_GROUP_BF16 - 1) / EXTRA_GROUP_BF16) * B * H;
+  const long s = 768 / groups;
+  return s < 1 ? 1 : (s > 4 ? 4 : static_cast<int>(s));
+}
+// Per query block and split, the words a split leaves for the combine: the two lanes' 32 keys
+// each (lane half h at 32h + 8q + e: entry e of list q), then the two lanes' sample counts.
+constexpr int SEED_SPLIT_WORDS = 68;
+static_assert(SEED_SPLIT_WORDS * 4 <= EXTRA_CAP * 2, "a split's words fit one candidate list");
 
-  const int nsteps = min(2 * P.M, min(4 * SAMPLE_STEPS, max(SAMPLE_STEPS, P.N / 1024)));
-  const int ntile = (nsteps + 1) / 2;
-  auto run_tok = [&](int s) { return sample_run(s < nsteps ? s : 0, nsteps, P.M); };
-  constexpr int OPS = TT::PT + 1;          // copies per thread per tile: keys, one flag dword
-  auto issue = [&](int it) {
-    T.issue(sm.k[it % NB], [&](int q) {
-      return std::make_pair(kbase + (int64_t)run_tok(2 * it + q) * P.k.sn, 32u * T.ksn_b);
-    });
-    F.issue_pair(run_tok(2 * it) >> 6, run_tok(2 * it + 1) >> 6, sm.fl[it % NB]);
-  };
-  uint32_t best[4][SAMPLE_KEEP];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int e = 0; e < SAMPLE_KEEP; ++e) best[q][e] = 0u;
-  int nsamp = 0;
-  for (int it = 0; it < NB - 1 && it < ntile; ++it) issue(it);
-#pragma unroll 1
-  for (int it = 0; it < ntile; ++it) {
-    wait_tiles<OPS>(min(NB - 2, ntile - 1 - it));
-    tile_barrier();
-    bool fl[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int s = 2 * it + q;
-      fl[q] = row_ok && s < nsteps && !FlagCopy::kept_pair(sm.fl[it % NB], q, run_tok(s) >> 6);
-    }
-    // the refill goes to the buffer every wave finished with before this tile's barrier
-    if (it + NB - 1 < ntile) issue(it + NB - 1);
-    if (wave_on) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const f32x16_t c = T.scores(sm.k[it % NB], q);
-        if (fl[q]) {
-          nsamp += 16;
-          // run 2 it + q goes to list (2 it + q) % 4
-          // insertion into a list kept in descending order: entry e of the new list is the
-          // median of old entries e-1 and e and the new key (one median-of-three per entry)
-          auto put = [&](uint32_t* bl) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const uint32_t k = float_key(c[r]);
-#pragma unroll
-              for (int e = SAMPLE_KEEP - 1; e > 0; --e) bl[e] = med3_u32(bl[e - 1], bl[e], k);
-              bl[0] = max(bl[0], k);
-            }
-          };
-          if (it & 1) put(best[2 + q]);
-          else put(best[q]);
-        }
-      }
-    }
-  }
-  if (!wave_on) return;
-  // the r-th best of the 64 kept keys of the query block (this lane's 32 and its partner's)
+// The seed of one query block from its lanes' best-of lists (this lane's and its partner's,
+// lane l ^ 32): the r-th best of the 64 kept keys.  Both lanes of the pair call it.
+__device__ __forceinline__ uint32_t seed_of_lists(const Problem& P, size_t row, bool row_ok,
+                                                  const uint32_t (&best)[4][SAMPLE_KEEP], int nsamp) {
   const int ntot = nsamp + __shfl_xor(nsamp, 32);
   const int ncand = P.N - P.bk * P.kept_cnt[row];
   uint32_t seed = 0u;
@@ -710,8 +647,147 @@ __global__ __launch_bounds__(256, 3) void extra_seed_kernel(Problem P) {
         if (cge >= r) seed = max(seed, v);
       }
   }
-  seed = max(seed, static_cast<uint32_t>(__shfl_xor(static_cast<int>(seed), 32)));
+  return max(seed, static_cast<uint32_t>(__shfl_xor(static_cast<int>(seed), 32)));
+}
+
+// Insertion into a best-of list kept in descending order: entry e of the new list is the median
+// of old entries e-1 and e and the new key (one median-of-three per entry).
+__device__ __forceinline__ void best_insert(uint32_t (&bl)[SAMPLE_KEEP], uint32_t k) {
+#pragma unroll
+  for (int e = SAMPLE_KEEP - 1; e > 0; --e) bl[e] = med3_u32(bl[e - 1], bl[e], k);
+  bl[0] = max(bl[0], k);
+}
+
+// Seeds: the sample runs (sample_run) scored for the group's 128 query blocks, two runs per
+// tile.  Each lane keeps the SAMPLE_KEEP best keys of every fourth run (four lists: list
+// 2 (t % 2) + q takes run q of tile t), so a query block's two lanes hold 64 of its best sample
+// keys; the seed is the r-th best of them, with r chosen so that about SAMPLE_MARGIN * E
+// candidates are expected at or above it.  A best-of-a-subset is at most the best of the whole
+// sample, so the seed only errs low (more candidates).  With S > 1 splits, split s takes tiles
+// s, s + S, ... and leaves its lists in the candidate-list buffer (not in use before the
+// sampled pass); extra_seed_combine_kernel merges the splits' lists, which gives every lane the
+// same lists as one workgroup over all tiles, so the seeds do not depend on S.
+template <int D>
+__global__ __launch_bounds__(256, 3) void extra_seed_kernel(Problem P) {
+  __shared__ ExtraSeedSmem<D> sm;
+  constexpr int NB = XNB_S;
+  using TT = ExtraTiles<D>;
+  const int S = seed_splits(P.B, P.H, P.Mq);
+  int unit, grp;
+  if (!xcd_unit(P.B * P.H * S, (P.Mq + EXTRA_GROUP_BF16 - 1) / EXTRA_GROUP_BF16, &unit, &grp)) return;
+  const int bh = unit / S, split = unit % S;
+  const int tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int rl = l % 32, i = grp * EXTRA_GROUP_BF16 + 32 * w + rl;
+  const int b = bh / P.H, h = bh % P.H;
+  const size_t row = (size_t)bh * P.Mq + (i < P.Mq ? i : 0);
+  const bool row_ok = i < P.Mq && !(i >= P.dense_q0 && i < P.dense_q1);
+  const uint16_t* kbase = static_cast<const uint16_t*>(P.k.p) + (int64_t)b * P.k.sb + (int64_t)h * P.k.sh;
+  TT T;
+  T.init(P, row, i < P.Mq);
+  FlagCopy F;
+  F.init(P, bh, i);
+  const bool wave_on = __ballot(row_ok) != 0;
+
+  const int nsteps = min(2 * P.M, min(4 * SAMPLE_STEPS, max(SAMPLE_STEPS, P.N / 1024)));
+  const int ntile = (nsteps + 1) / 2;
+  const int nmine = ntile > split ? (ntile - split + S - 1) / S : 0;   // this split's tiles
+  auto run_tok = [&](int s) { return sample_run(s < nsteps ? s : 0, nsteps, P.M); };
+  constexpr int OPS = TT::PT + 1;          // copies per thread per tile: keys, one flag dword
+  // local tile j is tile split + j S of the sample, in buffer j % NB
+  auto issue = [&](int j) {
+    const int it = split + j * S;
+    T.issue(sm.k[j % NB], [&](int q) {
+      return std::make_pair(kbase + (int64_t)run_tok(2 * it + q) * P.k.sn, 32u * T.ksn_b);
+    });
+    F.issue_pair(run_tok(2 * it) >> 6, run_tok(2 * it + 1) >> 6, sm.fl[j % NB]);
+  };
+  uint32_t best[4][SAMPLE_KEEP];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < SAMPLE_KEEP; ++e) best[q][e] = 0u;
+  int nsamp = 0;
+  for (int j = 0; j < NB - 1 && j < nmine; ++j) issue(j);
+#pragma unroll 1
+  for (int j = 0; j < nmine; ++j) {
+    const int it = split + j * S;
+    wait_tiles<OPS>(min(NB - 2, nmine - 1 - j));
+    tile_barrier();
+    bool fl[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int s = 2 * it + q;
+      fl[q] = row_ok && s < nsteps && !FlagCopy::kept_pair(sm.fl[j % NB], q, run_tok(s) >> 6);
+    }
+    // the refill goes to the buffer every wave finished with before this tile's barrier
+    if (j + NB - 1 < nmine) issue(j + NB - 1);
+    if (wave_on) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const f32x16_t c = T.scores(sm.k[j % NB], q);
+        if (fl[q]) {
+          nsamp += 16;
+          // run 2 it + q goes to list (2 it + q) % 4
+          auto put = [&](uint32_t (&bl)[SAMPLE_KEEP]) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) best_insert(bl, float_key(c[r]));
+          };
+          if (it & 1) put(best[2 + q]);
+          else put(best[q]);
+        }
+      }
+    }
+  }
+  if (!wave_on) return;
+  if (S > 1) {
+    if (i < P.Mq) {
+      uint32_t* out = reinterpret_cast<uint32_t*>(P.extra_buf + row * P.extra_lists * EXTRA_CAP) +
+                      split * SEED_SPLIT_WORDS;
+      const int h32 = l / 32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < SAMPLE_KEEP; ++e) out[32 * h32 + 8 * q + e] = best[q][e];
+      out[64 + h32] = static_cast<uint32_t>(nsamp);
+    }
+    return;
+  }
+  const uint32_t seed = seed_of_lists(P, row, row_ok, best, nsamp);
   if (l < 32 && i < P.Mq) P.extra_seed[row] = seed;
+}
+
+// The seeds from the splits' lists (seed_splits > 1): every lane inserts the other splits'
+// entries of each list into split 0's, then the seed is taken as in the one-split pass.
+__global__ __launch_bounds__(256) void extra_seed_combine_kernel(Problem P) {
+  const int S = seed_splits(P.B, P.H, P.Mq);
+  const int grp = blockIdx.x, bh = blockIdx.y, l = threadIdx.x % 64, w = threadIdx.x / 64;
+  const int i = grp * EXTRA_GROUP_BF16 + 32 * w + l % 32, h32 = l / 32;
+  if (i >= P.Mq) return;                                  // both lanes of a pair leave together
+  const size_t row = (size_t)bh * P.Mq + i;
+  const bool row_ok = !(i >= P.dense_q0 && i < P.dense_q1);
+  const uint32_t* in = reinterpret_cast<const uint32_t*>(P.extra_buf + row * P.extra_lists * EXTRA_CAP);
+  uint32_t best[4][SAMPLE_KEEP];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < SAMPLE_KEEP; ++e) best[q][e] = in[32 * h32 + 8 * q + e];
+  int nsamp = static_cast<int>(in[64 + h32]);
+  for (int sp = 1; sp < S; ++sp) {
+    const uint32_t* o = in + sp * SEED_SPLIT_WORDS;
+    uint32_t v[4][SAMPLE_KEEP];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < SAMPLE_KEEP; ++e) v[q][e] = o[32 * h32 + 8 * q + e];
+    nsamp += static_cast<int>(o[64 + h32]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < SAMPLE_KEEP; ++e) best_insert(best[q], v[q][e]);
+  }
+  const uint32_t seed = seed_of_lists(P, row, row_ok, best, nsamp);
+  if (l < 32) P.extra_seed[row] = seed;
 }
 
 // The threshold key thr as a float: a score c passes (float_key(c) >= thr) exactly when
@@ -1210,13 +1286,16 @@ hipError_t launch_extra_select(const Problem& P, hipStream_t stream) {
   dim3 grid((P.Mq + XR - 1) / XR, P.B * P.H, P.extra_slices);
   const int ngrp = (P.Mq + EXTRA_GROUP_BF16 - 1) / EXTRA_GROUP_BF16;
   dim3 g16(xcd_grid(P.B * P.H * P.extra_slices, ngrp));
-  dim3 gseed(xcd_grid(P.B * P.H, ngrp));
+  const int nsplit = seed_splits(P.B, P.H, P.Mq);
+  dim3 gseed(xcd_grid(P.B * P.H * nsplit, ngrp));
   dim3 g2(P.Mq, P.B * P.H);
   auto pass1 = [&](int repair) {
     if (P.dtype == 0) {
       if (!repair) {
         if (P.d == 128) hipLaunchKernelGGL(extra_seed_kernel<128>, gseed, dim3(256), 0, stream, P);
         else hipLaunchKernelGGL(extra_seed_kernel<64>, gseed, dim3(256), 0, stream, P);
+        if (nsplit > 1)
+          hipLaunchKernelGGL(extra_seed_combine_kernel, dim3(ngrp, P.B * P.H), dim3(256), 0, stream, P);
       }
       if (repair) {
         if (P.d == 128) hipLaunchKernelGGL((extra_tile_kernel<128, true>), g16, dim3(256), 0, stream, P);

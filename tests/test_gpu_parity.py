@@ -286,6 +286,46 @@ def test_extra_selection_overflow_goes_to_exact_pass():
     assert (sel["extra_cnt"] == 256).all()
 
 
+def test_seeds_do_not_depend_on_the_sample_split():
+    # The seeds' pass deals a group's sampled tiles to 1, 2 or 4 workgroups (about 768
+    # workgroups in all) and merges their best-of lists; the merged lists equal one workgroup's
+    # over all tiles, so each head's seeds must be bit for bit the same whether the head runs
+    # with 1, 191 or 383 other heads (N = 16384: 4, 2 and 1 splits), and so must its extra-token
+    # sets and output (the selection is exact whatever the seeds).
+    N, d = 16384, 128
+    x = random_qkv(1, 2, N, d, seed=21, dtype="bf16")
+    q2, k2, v2 = device_inputs(x)
+    kw = dict(tau=1.3, block_q=64, block_k=64, sink_range=256, extra_tokens=256,
+              dense_rows=(N - 1024, N), return_workspace=True)
+    seeds, outs, extras = [], [], []
+    for H in (2, 192, 384):
+        q, k, v = (t.repeat(1, H // 2, 1, 1).contiguous() for t in (q2, k2, v2))
+        print(f"\n[seed split] H={H}", flush=True)
+        out, ws = sa.sol_attn(q, k, v, **kw)
+        torch.cuda.synchronize()
+        L = sa.workspace_layout(sa.MODE_SOL, sa.BF16, 1, H, N, d, 64, 64)
+        seed = ws[L.extra_seed:L.extra_seed + 4 * H * L.Mq].view(torch.int32).view(H, L.Mq)
+        views = sa.selection_views(ws, sa.MODE_SOL, sa.BF16, 1, H, N, d, 64, 64)
+        seeds.append(seed[:2].cpu())
+        outs.append(out[:, :2].cpu())
+        extras.append((views["extra_cnt"][:2].cpu(), views["extra_idx"][:2].cpu(),
+                       views["extra_flag"][:2].cpu()))
+        del q, k, v, out, ws
+        torch.cuda.empty_cache()
+    sparse = seeds[0][:, :(N - 1024) // 64]
+    assert (sparse != 0).float().mean() > 0.99        # a seed for (nearly) every sparse block
+    for j in (1, 2):
+        assert torch.equal(seeds[j], seeds[0])
+        assert torch.equal(outs[j].view(torch.int16), outs[0].view(torch.int16))
+        # (which query blocks the exact pass takes may differ: the token slices of the sampled
+        # pass, and so its lists' capacity per token, depend on the head count)
+        cnt, idx, _ = extras[j]
+        assert torch.equal(cnt, extras[0][0])
+        # the lists' entries past each query block's count are not written
+        live = torch.arange(idx.shape[-1])[None, None, :] < cnt[..., None]
+        assert torch.equal(torch.where(live, idx, 0), torch.where(live, extras[0][1], 0))
+
+
 def test_batch_and_dense_rows_fp32():
     x = random_qkv(2, 2, 4096, 64, seed=9, dtype="fp32")
     w = workload(1, B=2, dense_rows=(3072, 4096), extra_tokens=64, sink_range=100)
