@@ -615,7 +615,7 @@ __host__ __device__ inline int seed_splits(int B, int H, int Mq) {
 // Per query block and split, the words a split leaves for the combine: the two lanes' 32 keys
 // each (lane half h at 32h + 8q + e: entry e of list q), then the two lanes' sample counts.
 constexpr int SEED_SPLIT_WORDS = 68;
-static_assert(SEED_SPLIT_WORDS * 4 <= EXTRA_CAP * 2, "a split's words fit one candidate list");
+static_assert(4 * SEED_SPLIT_WORDS <= EXTRA_CAP * 2, "four splits' words fit one candidate list");
 
 // The seed of one query block from its lanes' best-of lists (this lane's and its partner's,
 // lane l ^ 32): the r-th best of the 64 kept keys.  Both lanes of the pair call it.
