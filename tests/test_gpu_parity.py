@@ -326,6 +326,44 @@ def test_seeds_do_not_depend_on_the_sample_split():
         assert torch.equal(torch.where(live, idx, 0), torch.where(live, extras[0][1], 0))
 
 
+def test_block_constant_keys_and_values_tie_breaks_and_dense_limit():
+    # Every key block holds one key vector and one value vector 64 times.  The extra-token
+    # scores of a block's tokens are then equal bit for bit, so a cut inside a block (96 extra
+    # tokens: one and a half blocks' worth) must take its lowest-numbered tokens, as the
+    # oracle's (score desc, token asc) order says; and a skipped block's centroid term is
+    # exactly the sum over its tokens not taken as extra tokens, so the sparse output must
+    # equal dense attention on every row.
+    B, H, N, d = 1, 2, 8192, 128
+    rng = np.random.default_rng([31, 2])
+    q = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    kb = rng.standard_normal((B, H, N // 64, 1, d), dtype=np.float32)
+    k = np.broadcast_to(kb, (B, H, N // 64, 64, d)).reshape(B, H, N, d).copy()
+    vb = rng.standard_normal((B, H, N // 64, 1, d), dtype=np.float32)
+    v = np.broadcast_to(vb, (B, H, N // 64, 64, d)).reshape(B, H, N, d).copy()
+    bits = [bf16_round(a) for a in (q, k, v)]
+    w = Workload(0, "block-constant-keys", B=B, H=H, T=1, Hh=1, Ww=N, d=d, dtype="bf16", mode="sol",
+                 block_q=64, block_k=64, tau=1.3, extra_tokens=96, sink_range=64)
+    x = Inputs(w, tuple(range(H)), *[bf16_to_f32(b) for b in bits], *bits)
+    out, sel, rep = run_and_check(w, x, range(H), qblocks=[0, 1, 37, 127])
+    assert rep.mask_flips == 0 and rep.extra_flips == 0
+    # the cut falls inside a block for (nearly) every query block: its lowest tokens were taken
+    partial = 0
+    for bh in range(H):
+        for i in range(N // 64):
+            idx = np.sort(sel["extra_idx"][bh, i, :sel["extra_cnt"][bh, i]])
+            blocks, counts = np.unique(idx // 64, return_counts=True)
+            for j, c in zip(blocks, counts):
+                if c < 64:
+                    partial += 1
+                    assert (idx[idx // 64 == j] == 64 * j + np.arange(c)).all()
+    assert partial > 0
+    ref = np.stack([dense.dense_attention(x.q[0, h], x.k[0, h], x.v[0, h]) for h in range(H)])
+    err = np.abs(out[0] - ref)
+    print(f"[block-constant keys] dense limit: max {err.max():.3e} mean {err.mean():.3e}; "
+          f"partial blocks {partial}", flush=True)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
 def test_batch_and_dense_rows_fp32():
     x = random_qkv(2, 2, 4096, 64, seed=9, dtype="fp32")
     w = workload(1, B=2, dense_rows=(3072, 4096), extra_tokens=64, sink_range=100)
