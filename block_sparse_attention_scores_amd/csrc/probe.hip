@@ -1,6 +1,6 @@
 // Achievable-peak probes for the measurement of the library's kernels against their rooflines:
 // the chip's published peaks are the rooflines, and these loops measure what the matrix cores
-// and the memory system actually deliver on the box the bench runs on.
+// and the memory system actually deliver on the machine the bench runs on.
 //   kind 0: bf16 32x32x16 matrix instructions, four independent accumulators per wave, no memory
 //   kind 1: fp32 32x32x2 matrix instructions, likewise
 //   kind 2: device copy of bytes/2 bytes from the first half of buf to the second (16-byte

@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run in one process on the GPU machine; on a host without a GPU they are skipped,
+    # GPU tests run in one process on a host with the GPU; on a host without one they are skipped,
     # never silently rerouted.
     try:
         import torch
