@@ -368,8 +368,8 @@ def run_workload(w, a, torch, sa, dev, steps, warmup, keep_inputs=False):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this path shards by (batch, head) with no exchange; "
-              "multi-GPU runs are not part of this build", file=sys.stderr)
+        print("bench.py runs on one GPU only: the path shards by (batch, head) with no exchange, "
+              "and no multi-GPU run is measured", file=sys.stderr)
         sys.exit(2)
 
     import torch

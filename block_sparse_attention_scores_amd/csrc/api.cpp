@@ -113,9 +113,9 @@ int check(int mode, const void* q, const void* k, const void* v, void* out, int 
     if (lo < ohi && olo < hi) return fail(SOLATTN_EINVAL, "out overlaps %c", "qkv"[t]);
   }
 
-  if (d != 64 && d != 128) return fail(SOLATTN_ENOTSUP, "d=%d (this build: 64 or 128)", d);
-  if (block_k != 64) return fail(SOLATTN_ENOTSUP, "block_k=%d (this build: 64)", block_k);
-  if (block_q != 64 && block_q != 128) return fail(SOLATTN_ENOTSUP, "block_q=%d (this build: 64, 128)", block_q);
+  if (d != 64 && d != 128) return fail(SOLATTN_ENOTSUP, "d=%d (supported: 64 or 128)", d);
+  if (block_k != 64) return fail(SOLATTN_ENOTSUP, "block_k=%d (supported: 64)", block_k);
+  if (block_q != 64 && block_q != 128) return fail(SOLATTN_ENOTSUP, "block_q=%d (supported: 64, 128)", block_q);
   if (N % block_q || N % block_k) return fail(SOLATTN_ENOTSUP, "N=%d not a multiple of the block sizes", N);
   if (d0 % block_q || d1 % block_q) return fail(SOLATTN_ENOTSUP, "dense rows not block_q aligned");
   if (r0 % block_q || r1 % block_q) return fail(SOLATTN_ENOTSUP, "query-row window not block_q aligned");
@@ -568,7 +568,7 @@ const char* solattn_status_string(int status) {
   switch (status) {
     case SOLATTN_OK: return "ok";
     case SOLATTN_EINVAL: return "invalid argument";
-    case SOLATTN_ENOTSUP: return "not supported by this build";
+    case SOLATTN_ENOTSUP: return "not supported by the library";
     case SOLATTN_EWORKSPACE: return "workspace too small";
     case SOLATTN_EHIP: return "HIP runtime error";
     default: return "unknown status";

@@ -40,7 +40,7 @@ extern "C" {
 /* Status codes. */
 #define SOLATTN_OK          0
 #define SOLATTN_EINVAL     -1   /* an argument is out of its domain                        */
-#define SOLATTN_ENOTSUP    -2   /* valid, but this build does not implement the shape      */
+#define SOLATTN_ENOTSUP    -2   /* valid, but the library does not implement the shape     */
 #define SOLATTN_EWORKSPACE -3   /* the caller's workspace is smaller than required        */
 #define SOLATTN_EHIP       -4   /* a HIP runtime or launch error (see last_error_detail)   */
 
