@@ -91,3 +91,14 @@ def test_selection_check_counts_flips():
     ref["kept"][0, 2] = True
     out = bench.selection_check(w, sel, {0: ref})
     assert out["rows"] == 2 and out["mask_flips"] == 1 and out["extra_flips"] == 2
+
+
+def test_cpu_baseline_names_its_threads_and_blas():
+    # the oracle leg on a tiny sample: the fields the bench line reports beside the time
+    from gen import make_inputs
+    w = workload(1)
+    x = make_inputs(w, heads=[0])
+    cb, refs = bench.cpu_baseline(w, x, heads=(0,), n_sparse=2, n_dense=0)
+    assert cb["kind"] == "oracle" and cb["unit"] == "ms" and cb["value"] > 0
+    assert cb["cores"] >= 1 and cb["host_cpus"] >= 1 and cb["blas"]
+    assert 0 in refs and refs[0]["kept"].shape == (w.N // w.block_q, w.N // w.block_k)
