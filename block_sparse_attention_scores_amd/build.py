@@ -26,6 +26,14 @@ COMMON = [
 ]
 
 
+# Per-file compiler options, each measured against the default.  The extra-token selection
+# (bookkeeping between its matrix products) runs best under the max-ILP instruction scheduler:
+# 1.257 -> 1.235 ms at N = 65536, H = 24 (two alternating runs on one GPU).
+FILE_FLAGS = {
+    "extra.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def hipcc():
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -41,7 +49,7 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src.rsplit(".", 1)[0] + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [cc, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *COMMON, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
